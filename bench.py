@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Packed segment-id masked attention, fwd+bwd, on one MI355X.
+
+One step = the whole hot path over the 4 x 288-frame pack (episodes of
+119/177/285/239 valid frames padded to 288 frames, 32 tokens per frame ->
+36,864 tokens, 24 heads x 128, bf16): per-token seq ids from the valid frame
+counts, the block mask, the forward, and the backward (row sums, dQ, dK/dV).
+Inputs are synthetic (seeded, N(0,1)*0.5 bf16) and already resident in HBM.
+
+Prints ONE JSON line on stdout.  value = useful TFLOP/s = 14 * d * P * H /
+step time, where P counts only the allowed (same id, id >= 0) query-key pairs
+per head.  Per-stage times (HIP events on the stream the library launches on)
+go to stderr and into the JSON's "stages" object.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "masked-attn fwd+bwd useful TFLOP/s, 4×288-frame pack; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# algorithmic flops per allowed (query, key) pair per head, in units of head_dim
+FLOPS_PER_PAIR = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(spec, q, k, v, do, heads):
+    """Time the fp64 CPU oracle on a bounded sample (a subset of heads)."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import seqids as osid
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    ids = osid.seq_ids_from_valid_frames(spec.valid_frames, spec.frames_padded,
+                                         spec.q_tokens_per_frame)
+    t0 = time.perf_counter()
+    oatt.forward_backward(q, k, v, do, ids, ids, spec.scale, heads=heads)
+    dt = time.perf_counter() - t0
+    pairs = oatt.useful_pairs(ids, ids)
+    flops = 14.0 * spec.head_dim * pairs * len(heads)
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{spec.name}: fp64 fwd+bwd of heads {heads} of {spec.heads} "
+                      f"(all {spec.nq} tokens), useful flops 14*d*P per head"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload number (3 = the metric)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=str, default="0,23")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the packed path shards by whole packs, one per GPU, with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import packed_variable_length_amd as pa
+    import workloads as wl
+
+    spec = wl.config(args.config)
+    assert spec.dtype == "bf16" and spec.valid_frames is not None
+    log(f"[bench] workload {spec.name}: nq={spec.nq} heads={spec.heads} d={spec.head_dim}")
+    q, k, v, do = wl.make_values(spec)
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
+    Q, K, V, DO = T(q), T(k), T(v), T(do)
+    vf = torch.from_numpy(spec.valid_frames).to(dev)
+    H, d, nq = spec.heads, spec.head_dim, spec.nq
+    ids = torch.empty(nq, dtype=torch.int32, device=dev)
+    O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+    lse = torch.empty((H, nq), dtype=torch.float32, device=dev)
+    delta = torch.empty((H, nq), dtype=torch.float32, device=dev)
+    mstore = torch.empty(pa.build_block_mask_bytes(nq, nq, 128, 128), dtype=torch.uint8,
+                         device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ["seq_ids", "block_mask", "fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        pa.seq_ids_from_valid_frames(vf, spec.frames_padded, spec.q_tokens_per_frame, out=ids)
+        mark(1)
+        mask = pa.build_block_mask(ids, ids, 128, 128, storage=mstore)
+        mark(2)
+        pa.attn_packed_fwd(Q, K, V, ids, ids, mask, spec.scale, out=O, lse=lse)
+        mark(3)
+        pa.attn_packed_bwd_preprocess(O, DO, delta)
+        mark(4)
+        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, delta, ids, ids, mask, spec.scale, dq=dQ)
+        mark(5)
+        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, delta, ids, ids, mask, spec.scale, dk=dK,
+                                dv=dV)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    valid = ids_h[ids_h >= 0]
+    pairs = int((np.bincount(valid).astype(np.int64) ** 2).sum())  # self-attention pack
+    useful = 14.0 * d * pairs * H
+
+    # timed region: wall clock around exactly `steps` steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # per-stage HIP events over a second pass of the same steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                for j, n in enumerate(names)}
+    for n in names:
+        log(f"[bench] {n:10s} {stage_ms[n]:8.3f} ms")
+    tflops = useful / wall / 1e12
+    log(f"[bench] step {wall * 1e3:.3f} ms  useful {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    kernels = {n: stage_ms[n] for n in FLOPS_PER_PAIR}
+    dom = max(kernels, key=kernels.get)
+    achieved = FLOPS_PER_PAIR[dom] * d * pairs * H / (kernels[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_bf16_kernel<128>",
+                                            "bwd_dq": "dq_bf16_kernel<128>",
+                                            "bwd_dkdv": "dkdv_bf16_kernel<128>"}[dom],
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": FLOPS_PER_PAIR[dom] * d * pairs * H,
+                "avg_launch_ms": round(kernels[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        heads = [int(x) for x in args.cpu_heads.split(",")]
+        log(f"[bench] cpu baseline: oracle on heads {heads} ...")
+        cpu = cpu_baseline(spec, q, k, v, do, heads)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']} s")
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 bf16; stands in for FurnitureBench episodes)",
+        "config": {"workload": f"{spec.name}: 4 episodes of "
+                               f"{'/'.join(str(int(x)) for x in spec.valid_frames)} valid frames "
+                               f"padded to {spec.frames_padded}, 32 tokens/frame, "
+                               f"{nq} tokens, {H} heads x {d}",
+                   "tokens": nq, "heads": H, "head_dim": d, "valid_pairs_per_head": pairs,
+                   "useful_flops": useful, "parallelism": "single GPU"},
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {n: round(stage_ms[n], 4) for n in names},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

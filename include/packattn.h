@@ -1,0 +1,201 @@
+/*
+ * packattn.h -- C ABI of libpackattn.so: packed segment-id masked attention
+ * (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Several variable-length episodes are packed into one
+ * sequence; every token carries a segment id.  A query attends only to keys
+ * with the same id, and a negative id (padding frames past an episode's valid
+ * frames get -1) removes the token both as query and as key
+ * ("Furniture packing, variable length" report, implementation part;
+ * "LingBot-VA packing" report, section 2.1).  Rows with no allowed key come
+ * out as exact zeros with LSE = -inf, never NaN ("LingBot-VA packing" report,
+ * section 3.1 table).  The mask is built once, as per-tile block sparsity, and
+ * shared by forward and backward; a forward of another shape between the two
+ * must not silently corrupt the backward (same report, section 2.2), so both
+ * passes take the mask descriptor explicitly and check it.
+ *
+ * Conventions for every entry point:
+ *   - returns an int32 status: PA_OK (0) or a negative PA_ERR_* code;
+ *   - never allocates device memory, never synchronizes the device; all work
+ *     is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *   - every device buffer is owned by the caller; the library keeps no state
+ *     between calls and is safe to call from several host threads;
+ *   - argument errors are detected on the host before anything is launched;
+ *     a failed launch returns PA_ERR_HIP;
+ *   - tensors are contiguous row-major: q, o, dout, dq are [nq][heads][head_dim],
+ *     k, v, dk, dv are [nkv][heads][head_dim]; lse is [heads][nq] fp32.
+ *     Pointers to tensors must be 16-byte aligned.
+ */
+#ifndef PACKATTN_H
+#define PACKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,          /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = -2,         /* a size is out of range                              */
+  PA_ERR_DTYPE = -3,         /* unknown pa_dtype                                    */
+  PA_ERR_HEADDIM = -4,       /* head_dim not supported (64 or 128)                  */
+  PA_ERR_MASK_MISMATCH = -5, /* mask descriptor does not fit this call              */
+  PA_ERR_WORKSPACE = -6,     /* caller storage / workspace too small                */
+  PA_ERR_HIP = -7,           /* a HIP launch failed                                 */
+  PA_ERR_ALIGN = -8          /* a tensor pointer is not 16-byte aligned             */
+};
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_str(int32_t status);
+
+/*
+ * seq_ids_from_valid_frames -- per-token segment ids of a frame-padded pack
+ * ("LingBot-VA packing" report, section 2.1: frames at or past
+ * valid_frames[b] get -1, the other tokens of episode b get b).
+ *
+ *   valid_frames      device int32[B]; entries are clamped to [0, frames_padded]
+ *   B                 number of episodes, >= 0 (0 writes nothing)
+ *   frames_padded     padded frame count per episode, >= 1
+ *   tokens_per_frame  tokens per frame, >= 1
+ *   seq_id            device int32[B * frames_padded * tokens_per_frame], written;
+ *                     token order is episode, then frame, then token
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, or more than 2^31-1 tokens).
+ */
+int32_t seq_ids_from_valid_frames(const int32_t* valid_frames, int32_t B, int32_t frames_padded,
+                                  int32_t tokens_per_frame, int32_t* seq_id, void* stream);
+
+/*
+ * Block mask: the per-tile sparsity of the same-id predicate
+ * ("LingBot-VA packing" report, sections 1 and 2.2: a block mask built from the
+ * seq ids; blocks without an allowed pair are skipped).
+ *
+ * The query axis is cut into nq_tiles = ceil(nq/block_q) tiles and the key axis
+ * into nkv_tiles = ceil(nkv/block_kv) tiles; the last tile of an axis may be
+ * short.  tile_class[i*nkv_tiles + j] is 0 (empty: no allowed pair), 2 (full:
+ * all block_q*block_kv positions are allowed pairs; a short tile never is) or
+ * 1 (partial).  The CSR lists hold the non-empty tiles in ascending order:
+ * key tiles of query tile i are q_cols[q_ptr[i] .. q_ptr[i+1]), query tiles of
+ * key tile j are kv_rows[kv_ptr[j] .. kv_ptr[j+1]).  q_order / kv_order list
+ * the tiles by decreasing list length (ties by ascending index); the attention
+ * kernels use them to start the longest work first.
+ *
+ * All pointers in the descriptor point into the caller's `storage` buffer; the
+ * descriptor itself is host memory, filled by build_block_mask.
+ */
+typedef struct pa_block_mask {
+  int32_t nq, nkv, block_q, block_kv, nq_tiles, nkv_tiles;
+  uint8_t* tile_class; /* device [nq_tiles * nkv_tiles]                         */
+  int32_t* q_ptr;      /* device [nq_tiles + 1]                                 */
+  int32_t* q_cols;     /* device, capacity nq_tiles * nkv_tiles                 */
+  int32_t* kv_ptr;     /* device [nkv_tiles + 1]                                */
+  int32_t* kv_rows;    /* device, capacity nq_tiles * nkv_tiles                 */
+  int32_t* q_order;    /* device [nq_tiles]                                     */
+  int32_t* kv_order;   /* device [nkv_tiles]                                    */
+} pa_block_mask;
+
+/* Bytes of device storage build_block_mask needs for these sizes, or 0 if the
+ * sizes are invalid (nq, nkv >= 1; block sizes 16..1024; at most 16384 tiles
+ * per axis). */
+size_t build_block_mask_bytes(int32_t nq, int32_t nkv, int32_t block_q, int32_t block_kv);
+
+/*
+ *   q_seq_id, kv_seq_id  device int32[nq], int32[nkv]; any negative id is padding;
+ *                        ids need not be sorted or contiguous
+ *   block_q, block_kv    tile sizes, 16..1024
+ *   storage, bytes       caller device buffer of >= build_block_mask_bytes(...),
+ *                        256-byte aligned; its contents are overwritten
+ *   out                  host descriptor, filled on success
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_HIP.
+ */
+int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const int32_t* kv_seq_id,
+                         int32_t nkv, int32_t block_q, int32_t block_kv, void* storage,
+                         size_t bytes, pa_block_mask* out, void* stream);
+
+/*
+ * attn_packed_fwd -- O = softmax(scale * Q K^T, masked) V per head, over the
+ * allowed pairs only, and LSE = log sum exp of the allowed scaled scores
+ * (natural log, fp32).  Rows with no allowed key: O = 0, LSE = -inf.
+ * Work per query tile runs only over its non-empty key tiles; the elementwise
+ * mask is applied only on partial tiles.
+ *
+ *   dtype      PA_BF16 (bf16 in/out, fp32 accumulation; head_dim 64 or 128;
+ *              the mask must use 128 x 128 tiles) or PA_F32 (fp32 throughout;
+ *              head_dim 64 or 128; mask tiles of 32, 64 or 128 per axis)
+ *   nq, nkv    tokens on each side, >= 1; heads >= 1
+ *   scale      score scale (1/sqrt(head_dim) is the usual choice)
+ *   q, k, v    device tensors of `dtype`
+ *   q_seq_id, kv_seq_id  the ids the mask was built from
+ *   mask       descriptor from build_block_mask for (nq, nkv)
+ *   o          device [nq][heads][head_dim] of `dtype`, written
+ *   lse        device fp32 [heads][nq], written
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_HEADDIM,
+ *         PA_ERR_MASK_MISMATCH, PA_ERR_ALIGN, PA_ERR_HIP.
+ */
+int32_t attn_packed_fwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, int32_t head_dim,
+                        float scale, const void* q, const void* k, const void* v,
+                        const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                        const pa_block_mask* mask, void* o, float* lse, void* stream);
+
+/* Workspace bytes attn_packed_bwd needs (the fp32 row sums Delta = rowsum(dO*O),
+ * [heads][nq]), or 0 for invalid sizes. */
+size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
+                                       int32_t head_dim);
+
+/*
+ * attn_packed_bwd -- gradients of attn_packed_fwd for upstream gradient dout:
+ *   P = exp(scale*QK^T - LSE) on allowed pairs (0 elsewhere and on -inf rows),
+ *   Delta = rowsum(dout * o), dS = P * (dout V^T - Delta),
+ *   dq = scale dS K, dk = scale dS^T Q, dv = P^T dout.
+ * Rows of dq with no allowed key, and rows of dk/dv that no query selects, are
+ * exact zeros.  Arguments as for attn_packed_fwd, plus
+ *   o, lse      the forward's outputs
+ *   dout        device [nq][heads][head_dim] of `dtype`
+ *   dq, dk, dv  device outputs of `dtype`, written (all rows)
+ *   workspace   device buffer of >= attn_packed_bwd_workspace_bytes(...),
+ *               256-byte aligned, overwritten
+ * Errors: as attn_packed_fwd, plus PA_ERR_WORKSPACE.
+ */
+int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, int32_t head_dim,
+                        float scale, const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, const int32_t* q_seq_id,
+                        const int32_t* kv_seq_id, const pa_block_mask* mask, void* dq, void* dk,
+                        void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages attn_packed_bwd runs, callable one by one (same kernels,
+ * same results; a caller that times or overlaps the stages uses these):
+ *
+ * attn_packed_bwd_preprocess -- Delta[h][i] = sum_d dout[i][h][d] * o[i][h][d]
+ *   (fp32, [heads][nq]); the row term of the softmax gradient.
+ *   Errors: PA_ERR_DTYPE, PA_ERR_HEADDIM, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
+ *           PA_ERR_HIP.
+ * attn_packed_bwd_dq -- dq = scale * dS K, query-tile major, reads `delta`.
+ * attn_packed_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dout, key-tile major,
+ *   reads `delta`.
+ *   Both: arguments and errors as attn_packed_bwd; `delta` is the
+ *   preprocess output for the same o and dout.
+ */
+int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t heads, int32_t head_dim,
+                                   const void* o, const void* dout, float* delta, void* stream);
+int32_t attn_packed_bwd_dq(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
+                           int32_t head_dim, float scale, const void* q, const void* k,
+                           const void* v, const void* dout, const float* lse, const float* delta,
+                           const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                           const pa_block_mask* mask, void* dq, void* stream);
+int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
+                             int32_t head_dim, float scale, const void* q, const void* k,
+                             const void* v, const void* dout, const float* lse,
+                             const float* delta, const int32_t* q_seq_id,
+                             const int32_t* kv_seq_id, const pa_block_mask* mask, void* dk,
+                             void* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACKATTN_H */

@@ -1,0 +1,22 @@
+"""Packed segment-id masked attention for MI355X (gfx950).
+
+The compute path is the HIP library ``libpackattn.so`` (C ABI in
+``include/packattn.h``); :mod:`packed_variable_length_amd.packattn` is its thin
+Python binding.  Importing this package fails if the library is not built.
+"""
+from .packattn import (  # noqa: F401
+    PA_BF16,
+    PA_F32,
+    BlockMask,
+    PackAttnError,
+    attn_packed_bwd,
+    attn_packed_bwd_dkdv,
+    attn_packed_bwd_dq,
+    attn_packed_bwd_preprocess,
+    attn_packed_bwd_workspace_bytes,
+    attn_packed_fwd,
+    build_block_mask,
+    build_block_mask_bytes,
+    pa_status_str,
+    seq_ids_from_valid_frames,
+)

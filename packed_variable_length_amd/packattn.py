@@ -1,0 +1,316 @@
+"""Thin ctypes binding of libpackattn.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (``include/packattn.h``)
+and does no arithmetic of its own: it checks tensor placement, dtypes and
+shapes, allocates the outputs with torch (device memory and streams are all
+torch provides here), passes raw device pointers and the current HIP stream,
+and raises :class:`PackAttnError` on a negative status.  There is no CPU
+fallback: if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpackattn.so")
+
+PA_F32, PA_BF16 = 0, 1
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+class PackAttnError(RuntimeError):
+    """A negative status returned by libpackattn."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pa_status_str(status)} ({status})")
+
+
+class PaBlockMask(ctypes.Structure):
+    """Mirror of ``pa_block_mask`` (host descriptor of device storage)."""
+
+    _fields_ = [
+        ("nq", ctypes.c_int32), ("nkv", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+        ("nq_tiles", ctypes.c_int32), ("nkv_tiles", ctypes.c_int32),
+        ("tile_class", ctypes.c_void_p),
+        ("q_ptr", ctypes.c_void_p), ("q_cols", ctypes.c_void_p),
+        ("kv_ptr", ctypes.c_void_p), ("kv_rows", ctypes.c_void_p),
+        ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()' from the repository root)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    pm = ctypes.POINTER(PaBlockMask)
+    sig = {
+        "pa_status_str": (ctypes.c_char_p, [i32]),
+        "seq_ids_from_valid_frames": (i32, [vp, i32, i32, i32, vp, vp]),
+        "build_block_mask_bytes": (sz, [i32, i32, i32, i32]),
+        "build_block_mask": (i32, [vp, i32, vp, i32, i32, i32, vp, sz, pm, vp]),
+        "attn_packed_fwd": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, pm, vp, vp,
+                                  vp]),
+        "attn_packed_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "attn_packed_bwd": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  pm, vp, vp, vp, vp, sz, vp]),
+        "attn_packed_bwd_preprocess": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+        "attn_packed_bwd_dq": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, pm, vp, vp]),
+        "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, pm, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def pa_status_str(status: int) -> str:
+    return _lib.pa_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PackAttnError(status, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# --------------------------------------------------------------------- seq ids
+def seq_ids_from_valid_frames(valid_frames: torch.Tensor, frames_padded: int,
+                              tokens_per_frame: int, out: Optional[torch.Tensor] = None
+                              ) -> torch.Tensor:
+    """int32 ids ``[B * frames_padded * tokens_per_frame]`` on the same device."""
+    _need(valid_frames, "valid_frames", torch.int32)
+    B = valid_frames.numel()
+    n = B * int(frames_padded) * int(tokens_per_frame)
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=valid_frames.device)
+    _need(out, "out", torch.int32, valid_frames.device)
+    if out.numel() != n:
+        raise ValueError(f"out has {out.numel()} elements, expected {n}")
+    _check(_lib.seq_ids_from_valid_frames(valid_frames.data_ptr(), B, int(frames_padded),
+                                          int(tokens_per_frame), out.data_ptr(),
+                                          _stream(valid_frames)), "seq_ids_from_valid_frames")
+    return out
+
+
+# --------------------------------------------------------------------- block mask
+class BlockMask:
+    """Owns the device storage of a block mask and its C descriptor."""
+
+    def __init__(self, storage: torch.Tensor, desc: PaBlockMask):
+        self.storage = storage
+        self.desc = desc
+
+    @property
+    def nq_tiles(self) -> int:
+        return self.desc.nq_tiles
+
+    @property
+    def nkv_tiles(self) -> int:
+        return self.desc.nkv_tiles
+
+    def _view(self, ptr: int, n: int, dtype) -> torch.Tensor:
+        off = ptr - self.storage.data_ptr()
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.storage[off:off + nbytes].view(dtype)
+
+    def tile_class(self) -> torch.Tensor:
+        d = self.desc
+        return self._view(d.tile_class, d.nq_tiles * d.nkv_tiles, torch.uint8).view(
+            d.nq_tiles, d.nkv_tiles)
+
+    def csr(self):
+        """``(q_ptr, q_cols, kv_ptr, kv_rows)`` as device views (lists trimmed)."""
+        d = self.desc
+        q_ptr = self._view(d.q_ptr, d.nq_tiles + 1, torch.int32)
+        kv_ptr = self._view(d.kv_ptr, d.nkv_tiles + 1, torch.int32)
+        nnz_q = int(q_ptr[-1].item())
+        nnz_kv = int(kv_ptr[-1].item())
+        return (q_ptr, self._view(d.q_cols, nnz_q, torch.int32), kv_ptr,
+                self._view(d.kv_rows, nnz_kv, torch.int32))
+
+    def orders(self):
+        d = self.desc
+        return (self._view(d.q_order, d.nq_tiles, torch.int32),
+                self._view(d.kv_order, d.nkv_tiles, torch.int32))
+
+
+def build_block_mask_bytes(nq: int, nkv: int, block_q: int = 128, block_kv: int = 128) -> int:
+    return int(_lib.build_block_mask_bytes(int(nq), int(nkv), int(block_q), int(block_kv)))
+
+
+def build_block_mask(q_seq_id: torch.Tensor, kv_seq_id: torch.Tensor, block_q: int = 128,
+                     block_kv: int = 128, storage: Optional[torch.Tensor] = None) -> BlockMask:
+    _need(q_seq_id, "q_seq_id", torch.int32)
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q_seq_id.device)
+    nq, nkv = q_seq_id.numel(), kv_seq_id.numel()
+    nbytes = build_block_mask_bytes(nq, nkv, block_q, block_kv)
+    if nbytes == 0:
+        raise PackAttnError(-2, "build_block_mask_bytes")
+    if storage is None:
+        storage = torch.empty(nbytes, dtype=torch.uint8, device=q_seq_id.device)
+    desc = PaBlockMask()
+    _check(_lib.build_block_mask(q_seq_id.data_ptr(), nq, kv_seq_id.data_ptr(), nkv,
+                                 int(block_q), int(block_kv), storage.data_ptr(),
+                                 storage.numel(), ctypes.byref(desc), _stream(q_seq_id)),
+           "build_block_mask")
+    return BlockMask(storage, desc)
+
+
+# --------------------------------------------------------------------- attention
+def _attn_shapes(q, k, v):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [tokens, heads, head_dim]")
+    if k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float32 or all bfloat16")
+    return q.shape[0], k.shape[0], q.shape[1], q.shape[2]
+
+
+def attn_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_seq_id: torch.Tensor,
+                    kv_seq_id: torch.Tensor, mask: BlockMask, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Returns ``(o [nq, H, d] like q, lse [H, nq] float32)``."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, device=q.device)
+    _need(q_seq_id, "q_seq_id", torch.int32, q.device)
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device)
+    nq, nkv, H, d = _attn_shapes(q, k, v)
+    if q_seq_id.numel() != nq or kv_seq_id.numel() != nkv:
+        raise ValueError("seq id lengths do not match q / k")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", q.dtype, q.device)
+    _need(lse_t, "lse", torch.float32, q.device)
+    _check(_lib.attn_packed_fwd(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), q_seq_id.data_ptr(),
+                                kv_seq_id.data_ptr(), ctypes.byref(mask.desc), o.data_ptr(),
+                                lse_t.data_ptr(), _stream(q)), "attn_packed_fwd")
+    return o, lse_t
+
+
+def attn_packed_bwd_workspace_bytes(dtype: torch.dtype, nq: int, nkv: int, heads: int,
+                                    head_dim: int) -> int:
+    return int(_lib.attn_packed_bwd_workspace_bytes(_DTYPES[dtype], int(nq), int(nkv),
+                                                    int(heads), int(head_dim)))
+
+
+def attn_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    dout: torch.Tensor, lse: torch.Tensor, q_seq_id: torch.Tensor,
+                    kv_seq_id: torch.Tensor, mask: BlockMask, scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None, grads=None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Returns ``(dq, dk, dv)`` with the shapes and dtype of ``(q, k, v)``."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, q.dtype, q.device)
+    _need(lse, "lse", torch.float32, q.device)
+    _need(q_seq_id, "q_seq_id", torch.int32, q.device)
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device)
+    nq, nkv, H, d = _attn_shapes(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (H, nq):
+        raise ValueError("o / dout / lse shapes do not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+    nbytes = attn_packed_bwd_workspace_bytes(q.dtype, nq, nkv, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.attn_packed_bwd(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
+                                ctypes.byref(mask.desc), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(q)), "attn_packed_bwd")
+    return dq, dk, dv
+
+
+def attn_packed_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor,
+                               delta: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Delta ``[H, nq]`` float32 = row sums of ``dout * o``."""
+    _need(o, "o")
+    _need(dout, "dout", o.dtype, o.device)
+    if o.dtype not in _DTYPES or o.dim() != 3 or dout.shape != o.shape:
+        raise ValueError("o and dout must be matching [nq, H, d] float32/bfloat16 tensors")
+    nq, H, d = o.shape
+    if delta is None:
+        delta = torch.empty((H, nq), dtype=torch.float32, device=o.device)
+    _need(delta, "delta", torch.float32, o.device)
+    _check(_lib.attn_packed_bwd_preprocess(_DTYPES[o.dtype], nq, H, d, o.data_ptr(),
+                                           dout.data_ptr(), delta.data_ptr(), _stream(o)),
+           "attn_packed_bwd_preprocess")
+    return delta
+
+
+def attn_packed_bwd_dq(q, k, v, dout, lse, delta, q_seq_id, kv_seq_id, mask: BlockMask,
+                       scale: Optional[float] = None, dq: Optional[torch.Tensor] = None):
+    nq, nkv, H, d = _attn_shapes(q, k, v)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, name, q.dtype, q.device)
+    _need(lse, "lse", torch.float32, q.device)
+    _need(delta, "delta", torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check(_lib.attn_packed_bwd_dq(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
+                                   k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                   delta.data_ptr(), q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
+                                   ctypes.byref(mask.desc), dq.data_ptr(), _stream(q)),
+           "attn_packed_bwd_dq")
+    return dq
+
+
+def attn_packed_bwd_dkdv(q, k, v, dout, lse, delta, q_seq_id, kv_seq_id, mask: BlockMask,
+                         scale: Optional[float] = None, dk: Optional[torch.Tensor] = None,
+                         dv: Optional[torch.Tensor] = None):
+    nq, nkv, H, d = _attn_shapes(q, k, v)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, name, q.dtype, q.device)
+    _need(lse, "lse", torch.float32, q.device)
+    _need(delta, "delta", torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(_lib.attn_packed_bwd_dkdv(_DTYPES[q.dtype], nq, nkv, H, d, float(scale),
+                                     q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                     lse.data_ptr(), delta.data_ptr(), q_seq_id.data_ptr(),
+                                     kv_seq_id.data_ptr(), ctypes.byref(mask.desc),
+                                     dk.data_ptr(), dv.data_ptr(), _stream(q)),
+           "attn_packed_bwd_dkdv")
+    return dk, dv

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "packattn.h")
+LIB = os.path.join(ROOT, "packed_variable_length_amd", "libpackattn.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_HEADDIM = 0, -1, -2, -3, -4
+PA_ERR_MASK_MISMATCH, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_ALIGN = -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from packed_variable_length_amd import build as b  # noqa: WPS433 (build on demand)
+        b.build(verbose=False)
+    from packed_variable_length_amd import packattn  # loads the library, checks signatures
+    return packattn._lib
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\**([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("seq_ids_from_valid_frames", "build_block_mask", "build_block_mask_bytes",
+                 "attn_packed_fwd", "attn_packed_bwd", "attn_packed_bwd_workspace_bytes",
+                 "pa_status_str"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    from packed_variable_length_amd import packattn
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_HEADDIM,
+                 PA_ERR_MASK_MISMATCH, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_ALIGN):
+        s = packattn.pa_status_str(code)
+        assert s and s != "unknown status"
+    assert packattn.pa_status_str(-99) == "unknown status"
+
+
+def test_mask_bytes_validation(lib):
+    assert lib.build_block_mask_bytes(36864, 36864, 128, 128) > 0
+    assert lib.build_block_mask_bytes(0, 10, 128, 128) == 0
+    assert lib.build_block_mask_bytes(10, 10, 8, 128) == 0        # block too small
+    assert lib.build_block_mask_bytes(10, 10, 128, 2048) == 0     # block too large
+    assert lib.build_block_mask_bytes(16384 * 16 + 1, 10, 16, 16) == 0  # too many tiles
+    assert lib.attn_packed_bwd_workspace_bytes(1, 100, 100, 2, 128) >= 800
+    assert lib.attn_packed_bwd_workspace_bytes(1, 100, 100, 2, 96) == 0
+    assert lib.attn_packed_bwd_workspace_bytes(7, 100, 100, 2, 128) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails first
+
+
+def test_seq_ids_errors(lib):
+    assert lib.seq_ids_from_valid_frames(None, 3, 8, 4, FAKE, None) == PA_ERR_NULL
+    assert lib.seq_ids_from_valid_frames(FAKE, -1, 8, 4, FAKE, None) == PA_ERR_SHAPE
+    assert lib.seq_ids_from_valid_frames(FAKE, 3, 0, 4, FAKE, None) == PA_ERR_SHAPE
+    assert lib.seq_ids_from_valid_frames(FAKE, 3, 8, 0, FAKE, None) == PA_ERR_SHAPE
+    assert lib.seq_ids_from_valid_frames(FAKE, 1 << 20, 1 << 10, 1 << 10, FAKE, None) == PA_ERR_SHAPE
+    assert lib.seq_ids_from_valid_frames(None, 0, 8, 4, None, None) == PA_OK  # empty: no-op
+
+
+def test_block_mask_errors(lib):
+    from packed_variable_length_amd.packattn import PaBlockMask
+    d = PaBlockMask()
+    need = lib.build_block_mask_bytes(1000, 1000, 128, 128)
+    args = lambda **kw: dict(dict(q=FAKE, nq=1000, k=FAKE, nkv=1000, bq=128, bkv=128,  # noqa: E731
+                                  st=FAKE, nb=need, out=ctypes.byref(d)), **kw)
+    call = lambda a: lib.build_block_mask(a["q"], a["nq"], a["k"], a["nkv"], a["bq"], a["bkv"],  # noqa: E731
+                                          a["st"], a["nb"], a["out"], None)
+    assert call(args(q=None)) == PA_ERR_NULL
+    assert call(args(st=None)) == PA_ERR_NULL
+    assert call(args(nq=0)) == PA_ERR_SHAPE
+    assert call(args(bq=4)) == PA_ERR_SHAPE
+    assert call(args(nb=need - 1)) == PA_ERR_WORKSPACE
+    assert call(args(st=ctypes.c_void_p(0x100010))) == PA_ERR_ALIGN
+
+
+def _fake_mask(nq, nkv, bq=128, bkv=128):
+    from packed_variable_length_amd.packattn import PaBlockMask
+    d = PaBlockMask()
+    d.nq, d.nkv, d.block_q, d.block_kv = nq, nkv, bq, bkv
+    d.nq_tiles, d.nkv_tiles = -(-nq // bq), -(-nkv // bkv)
+    for f in ("tile_class", "q_ptr", "q_cols", "kv_ptr", "kv_rows", "q_order", "kv_order"):
+        setattr(d, f, 0x200000)
+    return d
+
+
+def _fwd(lib, dtype=1, nq=500, nkv=500, H=2, d=128, mask=None, q=FAKE, o=FAKE):
+    m = _fake_mask(500, 500) if mask is None else mask
+    return lib.attn_packed_fwd(dtype, nq, nkv, H, d, 0.1, q, FAKE, FAKE, FAKE, FAKE,
+                               ctypes.byref(m), o, FAKE, None)
+
+
+def test_attention_argument_errors(lib):
+    assert _fwd(lib, dtype=5) == PA_ERR_DTYPE
+    assert _fwd(lib, d=96) == PA_ERR_HEADDIM
+    assert _fwd(lib, H=0) == PA_ERR_SHAPE
+    assert _fwd(lib, q=None) == PA_ERR_NULL
+    assert _fwd(lib, q=ctypes.c_void_p(0x100008)) == PA_ERR_ALIGN
+    assert lib.attn_packed_fwd(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, FAKE, None) == PA_ERR_NULL
+
+
+def test_mask_shape_hazard_is_rejected(lib):
+    # a mask built for another shape (the packing report's forward/backward
+    # ordering hazard) is refused before anything runs
+    assert _fwd(lib, mask=_fake_mask(400, 500)) == PA_ERR_MASK_MISMATCH
+    assert _fwd(lib, mask=_fake_mask(500, 500, 64, 128)) == PA_ERR_MASK_MISMATCH   # bf16 needs 128
+    assert _fwd(lib, dtype=0, mask=_fake_mask(500, 500, 48, 64)) == PA_ERR_MASK_MISMATCH
+    m = _fake_mask(500, 500)
+    m.nq_tiles = 3
+    assert _fwd(lib, mask=m) == PA_ERR_MASK_MISMATCH
+    ws = lib.attn_packed_bwd_workspace_bytes(1, 500, 500, 2, 128)
+    bad = _fake_mask(500, 600)
+    assert lib.attn_packed_bwd(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, ws,
+                               None) == PA_ERR_MASK_MISMATCH
+    good = _fake_mask(500, 500)
+    assert lib.attn_packed_bwd(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, ws - 1,
+                               None) == PA_ERR_WORKSPACE

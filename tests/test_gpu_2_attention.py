@@ -1,0 +1,206 @@
+"""GPU parity of packed masked attention (forward and backward) with the fp64 oracle.
+
+Small packs are compared element by element on every head; the full-size
+workloads are compared on a sample of heads (the oracle computes those heads
+completely) and checked on all heads for finiteness and exact-zero rows.
+Tolerances: see tests/_helpers.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import attention as oatt
+from oracle import seqids as osid
+from tests._helpers import compare, compare_lse, host64, ids_dev, row_has_pair, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import packed_variable_length_amd as pa_mod
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return pa_mod
+
+
+def _ids_from_spec(pa, s):
+    """(oracle ids, GPU ids) built independently for each side."""
+    if s.segment_ids is not None:
+        return (s.segment_ids, s.segment_ids), (ids_dev(s.segment_ids), ids_dev(s.segment_ids))
+    qo = osid.seq_ids_from_valid_frames(s.valid_frames, s.frames_padded, s.q_tokens_per_frame)
+    ko = osid.seq_ids_from_valid_frames(s.valid_frames, s.frames_padded, s.kv_tokens_per_frame)
+    vf = ids_dev(s.valid_frames)
+    qg = pa.seq_ids_from_valid_frames(vf, s.frames_padded, s.q_tokens_per_frame)
+    kg = pa.seq_ids_from_valid_frames(vf, s.frames_padded, s.kv_tokens_per_frame)
+    return (qo, ko), (qg, kg)
+
+
+def _run_gpu(pa, q, k, v, do, qg, kg, dtype, scale, bq=128, bkv=128):
+    Q, K, V, DO = (to_dev(a, dtype) for a in (q, k, v, do))
+    mask = pa.build_block_mask(qg, kg, bq, bkv)
+    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask, scale)
+    dq, dk, dv = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, scale)
+    torch.cuda.synchronize()
+    return dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(dq),
+                dk=host64(dk), dv=host64(dv))
+
+
+def _check(got, ref, qo, ko, dtype, heads=None):
+    q_ok, k_ok = row_has_pair(qo, ko)
+    out = {}
+    out["o"] = compare("O", got["o"], ref["o"], q_ok, dtype, heads)
+    out["dq"] = compare("dQ", got["dq"], ref["dq"], q_ok, dtype, heads)
+    out["dk"] = compare("dK", got["dk"], ref["dk"], k_ok, dtype, heads)
+    out["dv"] = compare("dV", got["dv"], ref["dv"], k_ok, dtype, heads)
+    compare_lse(got["lse"], ref["lse"], heads)
+    return out
+
+
+def _spec(valid, fp, tq, tk, heads, d, dtype, seed):
+    return wl.PackSpec(f"case-{seed}", heads=heads, head_dim=d, dtype=dtype, seed=seed,
+                       value_std=0.5 if dtype == "bf16" else 1.0,
+                       valid_frames=np.array(valid, np.int32), frames_padded=fp,
+                       q_tokens_per_frame=tq, kv_tokens_per_frame=tk)
+
+
+SMALL = [
+    # valid frames, padded frames, q tok/frame, kv tok/frame, heads, head_dim
+    ([5, 9, 0, 3, 7], 9, 32, 32, 2, 128),   # 1440 tokens: 12 tiles, ragged tail, empty episode
+    ([5, 9, 3], 9, 6, 32, 2, 128),          # cross-attention, nq != nkv
+    ([4, 1, 6], 6, 32, 32, 3, 64),          # head_dim 64
+    ([17, 2], 20, 16, 16, 1, 128),          # partial tiles in the middle of the pack
+    ([3, 5, 2], 8, 4, 4, 1, 64),            # the tiny pack in bf16
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_bf16_small_packs_all_heads(pa, case):
+    valid, fp, tq, tk, H, d = SMALL[case]
+    s = _spec(valid, fp, tq, tk, H, d, "bf16", 10 + case)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    _check(got, ref, qo, ko, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bf16_interleaved_ids(pa, seed):
+    rng = np.random.default_rng(seed)
+    nq, nkv, H, d = 700, 650 if seed else 700, 2, 128
+    qo = rng.integers(-1, 5, nq).astype(np.int32)
+    ko = qo.copy() if seed == 0 else rng.integers(-1, 4, nkv).astype(np.int32)  # id 4: no keys
+    s = wl.PackSpec("interleaved", heads=H, head_dim=d, dtype="bf16", seed=seed, value_std=0.5,
+                    segment_ids=qo)
+    q, _, _, do = wl.make_values(s)
+    kk = wl.round_to_bf16(rng.standard_normal((nkv, H, d)).astype(np.float32) * 0.5)
+    vv = wl.round_to_bf16(rng.standard_normal((nkv, H, d)).astype(np.float32) * 0.5)
+    got = _run_gpu(pa, q, kk, vv, do, ids_dev(qo), ids_dev(ko), "bf16", s.scale)
+    ref = oatt.forward_backward(q, kk, vv, do, qo, ko, s.scale)
+    _check(got, ref, qo, ko, "bf16")
+
+
+def test_bf16_all_padding_pack(pa):
+    s = _spec([0, 0], 4, 32, 32, 2, 128, "bf16", 3)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
+    for name in ("o", "dq", "dk", "dv"):
+        assert (got[name] == 0).all()
+    assert np.isneginf(got["lse"]).all()
+
+
+def test_fp32_tiny_pack(pa):
+    s = wl.config(1)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    for bq, bkv in ((32, 32), (64, 64), (128, 128), (32, 128)):
+        got = _run_gpu(pa, q, k, v, do, qg, kg, "f32", s.scale, bq, bkv)
+        ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+        _check(got, ref, qo, ko, "f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_multi_tile_and_cross(pa, d):
+    for spec in (_spec([5, 9, 0, 3], 9, 16, 16, 2, d, "f32", 7),
+                 _spec([5, 9, 3], 9, 6, 32, 2, d, "f32", 8)):
+        q, k, v, do = wl.make_values(spec)
+        (qo, ko), (qg, kg) = _ids_from_spec(pa, spec)
+        got = _run_gpu(pa, q, k, v, do, qg, kg, "f32", spec.scale, 64, 32)
+        ref = oatt.forward_backward(q, k, v, do, qo, ko, spec.scale)
+        _check(got, ref, qo, ko, "f32")
+
+
+def test_no_leakage_across_episodes(pa):
+    # 24 tokens per frame: query and key tiles straddle two episodes' valid tokens
+    s = _spec([9, 7, 9, 8], 9, 24, 24, 2, 128, "bf16", 21)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    base = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
+    ep = qo == 1
+    q2, k2, v2, do2 = (a.copy() for a in (q, k, v, do))
+    for a in (q2, k2, v2, do2):
+        a[ep] = wl.round_to_bf16(a[ep] * 1.5 + 0.25)
+    pert = _run_gpu(pa, q2, k2, v2, do2, qg, kg, "bf16", s.scale)
+    for name in ("o", "dq", "dk", "dv"):
+        assert np.array_equal(pert[name][~ep], base[name][~ep]), name
+        assert not np.array_equal(pert[name][ep], base[name][ep]), name
+    assert np.array_equal(pert["lse"][:, ~ep], base["lse"][:, ~ep])
+
+
+def test_backward_deterministic_and_mask_hazard(pa):
+    s = _spec([5, 9, 3], 9, 32, 32, 2, 128, "bf16", 4)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    Q, K, V, DO = (to_dev(a, "bf16") for a in (q, k, v, do))
+    mask = pa.build_block_mask(qg, kg)
+    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask)
+    # a forward of another shape in between must not corrupt this backward
+    other = ids_dev(np.zeros(300, np.int32))
+    mask_other = pa.build_block_mask(other, other)
+    X = to_dev(np.zeros((300, 2, 128), np.float32), "bf16")
+    pa.attn_packed_fwd(X, X, X, other, other, mask_other)
+    with pytest.raises(pa.PackAttnError) as ei:
+        pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask_other)
+    assert ei.value.status == -5
+    g1 = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask)
+    g2 = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(g1[0]),
+               dk=host64(g1[1]), dv=host64(g1[2]))
+    _check(got, ref, qo, ko, "bf16")
+
+
+# ------------------------------------------------------------- full-size workloads
+def _full_size(pa, s, heads):
+    print(f"[full-size] {s.name} nq={s.nq} nkv={s.nkv} heads checked {heads}", flush=True)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
+    q_ok, k_ok = row_has_pair(qo, ko)
+    for name, ok in (("o", q_ok), ("dq", q_ok), ("dk", k_ok), ("dv", k_ok)):
+        assert np.isfinite(got[name]).all(), name
+        assert (got[name][~ok] == 0).all(), name
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale, heads=heads)
+    return _check(got, ref, qo, ko, "bf16", heads)
+
+
+def test_full_var_4x288(pa):
+    _full_size(pa, wl.config(3), [0, 23])
+
+
+def test_full_equal_4x120(pa):
+    _full_size(pa, wl.config(2), [5])
+
+
+def test_full_long_mixed_64k(pa):
+    _full_size(pa, wl.config(5), [11])
+
+
+def test_full_bucketed_largest_self_and_cross(pa):
+    _full_size(pa, wl.config(4), [0])
+    cross = max(wl.bucketed_sweep(cross=True), key=lambda p: p.nq)
+    _full_size(pa, cross, [17])
