@@ -64,7 +64,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = the metric)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=str, default="0,23")
+    ap.add_argument("--cpu-heads", type=str, default="0,1,2,3,4,5,6,7",
+                    help="heads the oracle baseline computes (a bounded sample)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -118,6 +121,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        del src, dst
     ids_h = ids.cpu().numpy()
     valid = ids_h[ids_h >= 0]
     pairs = int((np.bincount(valid).astype(np.int64) ** 2).sum())  # self-attention pack

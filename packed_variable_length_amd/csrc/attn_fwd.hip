@@ -24,29 +24,20 @@
 #include <math.h>
 
 #include "pa_common.h"
+#include "pa_tile.h"
 
 namespace {
 
 using namespace pa;
 
 // ------------------------------------------------------------------ bf16 MFMA
-template <int D>
-struct FwdBf16 {
-  static constexpr int kThreads = 256;
-  static constexpr int kBQ = 128;              // query rows per workgroup (= mask tile)
-  static constexpr int kBKV = 128;             // key rows per mask tile
-  static constexpr int kSub = 64;              // key rows per inner step
-  static constexpr int kKStride = D * 2 + 16;  // bytes per K row in LDS
-  static constexpr int kVStride = kSub * 2 + 8;  // bytes per V^T row in LDS
-  static constexpr int kKBytes = kSub * kKStride;
-  static constexpr int kVBytes = D * kVStride;
-  static constexpr int kIdBytes = kSub * 4;
-  static constexpr int kBuf = kKBytes + kVBytes + kIdBytes;
-  static constexpr int kKChunks = kSub * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int kVThreads = (kSub / 4) * (D / 8);    // threads holding a 4x8 V block
-  static constexpr int kDB = D / 32;                         // 32-wide d blocks
-  static constexpr int kKK = D / 16;                         // 16-deep k steps over d
-};
+constexpr int kFwdSub = 64;          // key rows per inner step
+constexpr int kFwdTile = 64 * kRowBytes;  // one 64-row LDS tile
+constexpr int kFwdStage = 2 * kFwdTile + 256;  // K tile, V tile, 64 key ids
+// Rescale threshold (log2 units): the running max is only raised when a new
+// score exceeds it by more than this, so exp2 arguments stay <= kLazy and the
+// O rescale is skipped for almost every step.
+constexpr float kLazy = 8.0f;
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -57,182 +48,138 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ q_cols,
                 const int32_t* __restrict__ q_order, int32_t nkt, uint16_t* __restrict__ o,
                 float* __restrict__ lse) {
-  using C = FwdBf16<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBuf];
+  constexpr int kDB = D / 32, kKK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kFwdStage];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int work = blockIdx.x / H, h = blockIdx.x - work * H;
   const int qt = q_order[work];
   const int beg = q_ptr[qt];
   const int nsub = 2 * (q_ptr[qt + 1] - beg);
   const size_t rs = (size_t)H * D;  // elements between consecutive tokens
+  const int hoff = h * D;
 
-  const int qrow = qt * C::kBQ + wv * 32 + col;
+  const int qrow = qt * 128 + wv * 32 + col;
   const bool qin = qrow < nq;
-  const int qtag = qin ? query_tag(q_ids[qrow]) : kPadQuery;
+  const int qid = qin ? q_ids[qrow] : -1;
+  const bool qvalid = qid >= 0;
 
-  bf16x8 qf[C::kKK];
+  bf16x8 qf[kKK];
   {
-    const uint16_t* qp = q + (size_t)(qin ? qrow : nq - 1) * rs + h * D + 8 * hi;
+    const uint16_t* qp = q + (size_t)(qin ? qrow : nq - 1) * rs + hoff + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < C::kKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+    for (int kk = 0; kk < kKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+  }
+  int koff[kKK], voff[kDB][2];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) koff[kk] = row_off(lane, kk);
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    voff[db][0] = kFwdTile + tr_off(lane, db, 0);
+    voff[db][1] = kFwdTile + tr_off(lane, db, 1);
   }
 
-  f32x16 oacc[C::kDB];
+  f32x16 oacc[kDB];
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  if (nsub > 0) {
-    u32x4 kreg[C::kKChunks];
-    u32x4 vreg[4];
-    int32_t idreg = kPadKey;
+  auto stage = [&](int s) {
+    const int kt = q_cols[beg + (s >> 1)];
+    const int k0 = kt * 128 + (s & 1) * kFwdSub;
+    char* base = smem + (s & 1) * kFwdStage;
+    stage_tile<D, kFwdSub, 4>(k, rs, hoff, k0, nkv, base, wv, lane);
+    stage_tile<D, kFwdSub, 4>(v, rs, hoff, k0, nkv, base + kFwdTile, wv, lane);
+    if (wv == 0) stage_words(kv_ids, k0, nkv, base + 2 * kFwdTile, lane);
+  };
 
-    auto gload = [&](int s) {
-      const int kt = q_cols[beg + (s >> 1)];
-      const int k0 = kt * C::kBKV + (s & 1) * C::kSub;
-#pragma unroll
-      for (int i = 0; i < C::kKChunks; ++i) {
-        const int c = tid + C::kThreads * i;
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        const int kr = min(k0 + row, nkv - 1);
-        kreg[i] = *(const u32x4*)(k + (size_t)kr * rs + h * D + c8 * 8);
-      }
-      if (tid < C::kVThreads) {
-        const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int vr = min(k0 + 4 * kg + r, nkv - 1);
-          vreg[r] = *(const u32x4*)(v + (size_t)vr * rs + h * D + dc * 8);
-        }
-      }
-      if (tid < C::kSub) {
-        const int kr = k0 + tid;
-        idreg = kr < nkv ? key_tag(kv_ids[kr]) : kPadKey;
-      }
-    };
-    auto lstore = [&](int buf) {
-      char* kl = smem + buf * C::kBuf;
-      char* vl = kl + C::kKBytes;
-      int32_t* il = (int32_t*)(vl + C::kVBytes);
-#pragma unroll
-      for (int i = 0; i < C::kKChunks; ++i) {
-        const int c = tid + C::kThreads * i;
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        *(u32x4*)(kl + row * C::kKStride + c8 * 16) = kreg[i];
-      }
-      if (tid < C::kVThreads) {
-        const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int w = c >> 1, sh = (c & 1) * 16;
-          const uint32_t x0 = (vreg[0][w] >> sh) & 0xFFFFu, x1 = (vreg[1][w] >> sh) & 0xFFFFu;
-          const uint32_t x2 = (vreg[2][w] >> sh) & 0xFFFFu, x3 = (vreg[3][w] >> sh) & 0xFFFFu;
-          u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *(u32x2*)(vl + (8 * dc + c) * C::kVStride + 8 * kg) = pk;
-        }
-      }
-      if (tid < C::kSub) il[tid] = idreg;
-    };
+  if (nsub > 0) stage(0);
+  for (int s = 0; s < nsub; ++s) {
+    wait_vmem();
+    __syncthreads();  // stage s is in LDS; every wave is done with stage s - 1
+    if (s + 1 < nsub) stage(s + 1);
+    const int kt = q_cols[beg + (s >> 1)];
+    const int k0 = kt * 128 + (s & 1) * kFwdSub;
+    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
+    const char* base = smem + (s & 1) * kFwdStage;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < nsub; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nsub) gload(s + 1);
-      const int kt = q_cols[beg + (s >> 1)];
-      const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-      const char* kl = smem + buf * C::kBuf;
-      const char* vl = kl + C::kKBytes;
-      const int32_t* il = (const int32_t*)(vl + C::kVBytes);
-
-      // S^T = K Q^T for 64 keys (two 32-key blocks) x this wave's 32 queries
-      f32x16 sacc[2];
+    // S^T = K Q^T: 64 keys (two 32-key blocks) x this wave's 32 queries; lane
+    // holds keys 32mb + 8(j/4) + 4hi + j%4 of query `col`
+    f32x16 sacc[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[mb][j] = 0.f;
-        const char* krow = kl + (mb * 32 + col) * C::kKStride + 16 * hi;
+      for (int j = 0; j < 16; ++j) sacc[mb][j] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < C::kKK; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(krow + 32 * kk);
-          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[mb], 0, 0, 0);
-        }
-      }
-      // lane holds keys mb*32 + 8*(j/4) + 4*hi + j%4 of query `col`
+      for (int kk = 0; kk < kKK; ++kk)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            lds_row8(base, koff[kk] + 8192 * mb), qf[kk], sacc[mb], 0, 0, 0);
+    }
+    if (partial) {
+      const int32_t* il = (const int32_t*)(base + 2 * kFwdTile);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[mb][j] *= s2;
-      if (partial) {
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = mb * 32 + 8 * g + 4 * hi;
+          const int4 t4 = *(const int4*)(il + r0);
+          const int lim = nkv - k0 - r0;  // keys r0 + e with e >= lim are past the end
+          // branch-free: bitwise & of the three conditions, then a select
+          const bool ok0 = qvalid & (t4.x == qid) & (lim > 0);
+          const bool ok1 = qvalid & (t4.y == qid) & (lim > 1);
+          const bool ok2 = qvalid & (t4.z == qid) & (lim > 2);
+          const bool ok3 = qvalid & (t4.w == qid) & (lim > 3);
+          sacc[mb][4 * g + 0] = ok0 ? sacc[mb][4 * g + 0] : -INFINITY;
+          sacc[mb][4 * g + 1] = ok1 ? sacc[mb][4 * g + 1] : -INFINITY;
+          sacc[mb][4 * g + 2] = ok2 ? sacc[mb][4 * g + 2] : -INFINITY;
+          sacc[mb][4 * g + 3] = ok3 ? sacc[mb][4 * g + 3] : -INFINITY;
+        }
+    }
+    // online softmax on raw scores (scale folded into the exp2 argument)
+    float mx = sacc[0][0];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int4 t4 = *(const int4*)(il + mb * 32 + 8 * g + 4 * hi);
-            if (t4.x != qtag) sacc[mb][4 * g + 0] = -INFINITY;
-            if (t4.y != qtag) sacc[mb][4 * g + 1] = -INFINITY;
-            if (t4.z != qtag) sacc[mb][4 * g + 2] = -INFINITY;
-            if (t4.w != qtag) sacc[mb][4 * g + 3] = -INFINITY;
-          }
-      }
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * s2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
       const float mnew = fmaxf(m, mx);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m - muse);
-      float ps = 0.f;
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(sacc[mb][j] - muse);
-          sacc[mb][j] = p;
-          ps += p;
-        }
-      lsum = lsum * alpha + ps;
-      m = mnew;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
+      for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-
-      // P^T as bf16 B operands: slice kb covers keys 16kb..16kb+15
-      bf16x8 pb[4];
+      m = mnew;
+    }
+    const float nm = m == -INFINITY ? 0.f : -m;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int mb = kb >> 1, b0 = (kb & 1) * 8;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][b0 + e], s2, nm));
+        lsum += p[e];
+      }
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+      pb[kb] = __builtin_bit_cast(bf16x8, w);
+    }
+    // O^T += V^T P^T, V^T read transposed from the row-major V tile
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int mb = kb >> 1, b0 = (kb & 1) * 8;
-        u32x4 w;
-        w[0] = pack_bf16x2(sacc[mb][b0 + 0], sacc[mb][b0 + 1]);
-        w[1] = pack_bf16x2(sacc[mb][b0 + 2], sacc[mb][b0 + 3]);
-        w[2] = pack_bf16x2(sacc[mb][b0 + 4], sacc[mb][b0 + 5]);
-        w[3] = pack_bf16x2(sacc[mb][b0 + 6], sacc[mb][b0 + 7]);
-        pb[kb] = __builtin_bit_cast(bf16x8, w);
+        const bf16x8 a = join8(lds_tr4(base, voff[db][0] + 4096 * kb),
+                               lds_tr4(base, voff[db][1] + 4096 * kb));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], oacc[db], 0, 0, 0);
       }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const char* vrow = vl + (db * 32 + col) * C::kVStride + 8 * hi;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const u32x2 lo = *(const u32x2*)(vrow + 32 * kb);
-          const u32x2 up = *(const u32x2*)(vrow + 32 * kb + 16);
-          const u32x4 w = {lo[0], lo[1], up[0], up[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                             pb[kb], oacc[db], 0, 0, 0);
-        }
-      }
-      if (s + 1 < nsub) lstore(buf ^ 1);
-      __syncthreads();
-    }
   }
 
   // epilogue: both half-waves hold partial sums of the same query
@@ -240,16 +187,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const bool any = ltot > 0.f;
   const float inv = any ? 1.f / ltot : 0.f;
   if (qin) {
-    uint16_t* op = o + (size_t)qrow * rs + h * D;
+    uint16_t* op = o + (size_t)qrow * rs + hoff;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 pk = {0u, 0u};
-        if (any) {
-          pk[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-          pk[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        }
+        // rows without an allowed key have an all-zero accumulator and inv = 0
+        u32x2 pk;
+        pk[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        pk[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
         *(u32x2*)(op + db * 32 + 8 * g + 4 * hi) = pk;
       }
     if (hi == 0) lse[(size_t)h * nq + qrow] = any ? (m + log2f(ltot)) * kLn2 : -INFINITY;

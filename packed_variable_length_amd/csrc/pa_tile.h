@@ -1,0 +1,112 @@
+// LDS tile helpers for the bf16 MFMA kernels (gfx950).
+//
+// A tile holds up to 64 token rows of one head; each row is 256 bytes (128 bf16,
+// a 64-wide row uses the first half) split into 16 chunks of 16 bytes.  Chunk c
+// of row r is stored at chunk position c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4.
+// With this swizzle both access patterns the kernels use are free of LDS bank
+// conflicts:
+//   * row reads: 16 lanes read the same logical chunk of 16 consecutive rows
+//     (an MFMA operand whose contraction index runs along the row) -- swz is a
+//     bijection on any 16 consecutive rows starting at a multiple of 16;
+//   * transposed reads (ds_read_b64_tr_b16): 16 lanes read 4 consecutive rows x
+//     4 consecutive chunks -- the row's low bits move the chunk's high bits, so
+//     the 16 chunks land in 16 distinct positions.
+// Tiles are filled with direct global->LDS loads (global_load_lds_dwordx4): one
+// wave instruction writes 1 KB = 4 rows, lane i the 16 bytes at offset 16*i; the
+// swizzle is applied on the global side by choosing which chunk lane i fetches.
+#pragma once
+
+#include "pa_common.h"
+
+namespace pa {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_cvoid;
+
+constexpr int kRowBytes = 256;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ int tile_byte(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+}
+
+// Wave-uniform index of the calling wave inside its workgroup (kept in an SGPR).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Copy token rows row0 .. row0 + NROWS - 1 of head `h` (tensor [n][H][D] bf16,
+// `rs` elements between tokens) into an LDS tile.  Rows at or past n re-read
+// row n - 1; callers mask those positions.  NW waves share the work.
+template <int D, int NROWS, int NW>
+__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ g, size_t rs, int hoff,
+                                           int row0, int n, char* tile, int wv, int lane) {
+  static_assert(NROWS % 4 == 0, "tile rows come in groups of 4");
+  const int p = lane & 15;
+#pragma unroll
+  for (int blk = wv; blk < NROWS / 4; blk += NW) {
+    const int r = blk * 4 + (lane >> 4);
+    int c = p ^ swz(r);
+    if (D == 64) c &= 7;  // 64-wide rows use chunks 0..7; other slots get a spare copy
+    const int gr = min(row0 + r, n - 1);
+    const uint16_t* src = g + (size_t)gr * rs + hoff + c * 8;
+    __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(tile + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Copy `count` (<= 64) consecutive 32-bit values starting at src[i0] (clamped to
+// src[n - 1]) into LDS; one wave instruction, lane i writes dst[i].
+__device__ __forceinline__ void stage_words(const void* __restrict__ src, int i0, int n,
+                                            char* dst, int lane) {
+  const int i = min(i0 + lane, n - 1);
+  __builtin_amdgcn_global_load_lds((global_cvoid*)((const uint32_t*)src + i), (lds_void*)dst, 4,
+                                   0, 0);
+}
+
+// Wait for this wave's outstanding direct-to-LDS loads.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+__device__ __forceinline__ bf16x8 lds_row8(const char* tile, int byte) {
+  return *(const bf16x8*)(tile + byte);
+}
+
+__device__ __forceinline__ i16x4 lds_tr4(const char* tile, int byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tile + byte));
+}
+
+__device__ __forceinline__ bf16x8 join8(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v;
+  v.lo = lo;
+  v.hi = hi;
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane byte offsets (within a tile) of the MFMA operand reads.
+//
+// Row operand (32x32x16 A or B, contraction along the row): lane l reads row
+// 32*mb + (l % 32), logical chunk 2*kk + l/32.  The swizzle of such a row does
+// not depend on mb, so row_off(kk) + 8192*mb is the byte offset.
+__device__ __forceinline__ int row_off(int lane, int kk) {
+  const int r = lane & 31;
+  return r * kRowBytes + (((2 * kk + (lane >> 5)) ^ swz(r)) << 4);
+}
+
+// Transposed operand via ds_read_b64_tr_b16: the 16 lanes of a group together
+// fetch rows k0 .. k0+3 (4 bytes... 8 bytes per lane) and return, to lane L of
+// the group, the 4 values of column m0 + L at rows k0 .. k0+3.  For the 32x32x16
+// A operand (m = l % 32, 8 contraction slots per lane) with the contraction
+// slots mapped to rows {16kb + 4h + 0..3, 16kb + 8 + 4h + 0..3} (h = l / 32),
+// lane l supplies row 16kb + 4h + (L/4) (+8 for the second read) and columns
+// 32*db + 16*((l/16)%2) + 4*(L%4).  The swizzle of those rows does not depend
+// on kb, so tr_off(db, s) + 4096*kb is the byte offset (s = first/second read).
+__device__ __forceinline__ int tr_off(int lane, int db, int s) {
+  const int L = lane & 15, h = lane >> 5, gm = (lane >> 4) & 1;
+  const int row = 4 * h + (L >> 2) + 8 * s;
+  const int col = 32 * db + 16 * gm + 4 * (L & 3);  // element index in the row
+  return row * kRowBytes + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+}
+
+}  // namespace pa
