@@ -93,11 +93,12 @@ def main():
     ids = torch.empty(nq, dtype=torch.int32, device=dev)
     O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
     lse = torch.empty((H, nq), dtype=torch.float32, device=dev)
-    delta = torch.empty((H, nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(pa.attn_packed_bwd_workspace_bytes(torch.bfloat16, nq, nq, H, d),
+                     dtype=torch.uint8, device=dev)
     mstore = torch.empty(pa.build_block_mask_bytes(nq, nq, 128, 128), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream(dev)
-    names = ["seq_ids", "block_mask", "fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+    names = ["seq_ids", "block_mask", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv"]
 
     def step(ev=None):
         def mark(i):
@@ -110,12 +111,11 @@ def main():
         mark(2)
         pa.attn_packed_fwd(Q, K, V, ids, ids, mask, spec.scale, out=O, lse=lse)
         mark(3)
-        pa.attn_packed_bwd_preprocess(O, DO, delta)
+        pa.attn_packed_bwd_preprocess(O, DO, lse, ws)
         mark(4)
-        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, delta, ids, ids, mask, spec.scale, dq=dQ)
+        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, ws, ids, ids, mask, spec.scale, dq=dQ)
         mark(5)
-        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, delta, ids, ids, mask, spec.scale, dk=dK,
-                                dv=dV)
+        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, ids, ids, mask, spec.scale, dk=dK, dv=dV)
         mark(6)
 
     for _ in range(args.warmup):

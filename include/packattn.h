@@ -141,8 +141,8 @@ int32_t attn_packed_fwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, i
                         const int32_t* q_seq_id, const int32_t* kv_seq_id,
                         const pa_block_mask* mask, void* o, float* lse, void* stream);
 
-/* Workspace bytes attn_packed_bwd needs (the fp32 row sums Delta = rowsum(dO*O),
- * [heads][nq]), or 0 for invalid sizes. */
+/* Workspace bytes attn_packed_bwd needs (fp32 Delta = rowsum(dO*O) and the LSE in
+ * log2 units, each [heads][nq]), or 0 for invalid sizes. */
 size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                                        int32_t head_dim);
 
@@ -168,31 +168,35 @@ int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, i
 
 /*
  * The three stages attn_packed_bwd runs, callable one by one (same kernels,
- * same results; a caller that times or overlaps the stages uses these):
+ * same results; for callers that time or overlap the stages).  `workspace` is
+ * a device buffer of >= attn_packed_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned, that the preprocess fills and the other two stages read.
  *
- * attn_packed_bwd_preprocess -- Delta[h][i] = sum_d dout[i][h][d] * o[i][h][d]
- *   (fp32, [heads][nq]); the row term of the softmax gradient.
+ * attn_packed_bwd_preprocess -- the row terms of the softmax gradient:
+ *   Delta[h][i] = sum_d dout[i][h][d] * o[i][h][d] (fp32) and the forward's LSE
+ *   in log2 units (+inf on rows without an allowed key, so that P = 0 there).
  *   Errors: PA_ERR_DTYPE, PA_ERR_HEADDIM, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
- *           PA_ERR_HIP.
- * attn_packed_bwd_dq -- dq = scale * dS K, query-tile major, reads `delta`.
- * attn_packed_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dout, key-tile major,
- *   reads `delta`.
- *   Both: arguments and errors as attn_packed_bwd; `delta` is the
- *   preprocess output for the same o and dout.
+ *           PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * attn_packed_bwd_dq -- dq = scale * dS K, one workgroup per query tile.
+ * attn_packed_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dout, one workgroup
+ *   per key tile.
+ *   Both: arguments and errors as attn_packed_bwd.
  */
 int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t heads, int32_t head_dim,
-                                   const void* o, const void* dout, float* delta, void* stream);
+                                   const void* o, const void* dout, const float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 int32_t attn_packed_bwd_dq(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                            int32_t head_dim, float scale, const void* q, const void* k,
-                           const void* v, const void* dout, const float* lse, const float* delta,
+                           const void* v, const void* dout, const float* lse,
+                           const void* workspace, size_t workspace_bytes,
                            const int32_t* q_seq_id, const int32_t* kv_seq_id,
                            const pa_block_mask* mask, void* dq, void* stream);
 int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                              int32_t head_dim, float scale, const void* q, const void* k,
                              const void* v, const void* dout, const float* lse,
-                             const float* delta, const int32_t* q_seq_id,
-                             const int32_t* kv_seq_id, const pa_block_mask* mask, void* dk,
-                             void* dv, void* stream);
+                             const void* workspace, size_t workspace_bytes,
+                             const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                             const pa_block_mask* mask, void* dk, void* dv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,24 +11,31 @@
 // section 2.2); rows with no allowed pair get exact zero gradients.
 //
 // Three launches, none with atomics:
-//   delta    Delta = rowsum(dO * O)  (HBM-bound)
-//   dq       query-major, one 128-row query tile per workgroup: S^T = K Q^T,
-//            dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (query index along the lanes)
-//   dkdv     key-major, one 128-row key tile per workgroup: S = Q K^T,
-//            dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS (key index along
-//            the lanes, dK and dV accumulated in registers)
+//   preprocess  Delta = rowsum(dO * O) and LSE in log2 units (+inf on rows
+//               without an allowed key, so exp2 gives P = 0 there); HBM-bound
+//   dq          query-major, one 128-row query tile per workgroup: S^T = K Q^T,
+//               dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (query index on the lanes)
+//   dkdv        key-major, one 128-row key tile per workgroup: S = Q K^T,
+//               dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS (key index on
+//               the lanes, dK and dV accumulated in registers)
 // Splitting dQ from dK/dV recomputes S and dP once more (14 instead of 10
 // d*pairs flops per head) but needs no fp32 atomics, no zero-filled accumulator
 // and no conversion pass, and is deterministic.
+//
+// The bf16 kernels stage K/V (dq) or Q/dO (dkdv) tiles in swizzled LDS with
+// direct global->LDS loads; the operands whose contraction runs across rows
+// (K^T, Q^T, dO^T) are read with ds_read_b64_tr_b16 from the same row-major
+// tiles (see pa_tile.h).
 #include <math.h>
 
 #include "pa_common.h"
+#include "pa_tile.h"
 
 namespace {
 
 using namespace pa;
 
-// ------------------------------------------------------------------ delta
+// ------------------------------------------------------------------ preprocess
 template <typename T>
 __device__ __forceinline__ void load16(const T* p, float* out);
 
@@ -55,172 +62,137 @@ __device__ __forceinline__ void load16<float>(const float* p, float* out) {
   }
 }
 
-// 8 threads per (token, head) row of D = 128 (16 elements each) or 4 threads
-// for D = 64; the row sum is reduced with lane exchanges.
+// Block = 256 / (D/16) consecutive query rows of one head (D/16 threads per
+// row, 16 elements each), so both outputs are written coalesced.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
-delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, int32_t nq, int32_t H,
-             float* __restrict__ delta) {
-  constexpr int kPer = D / 16;  // threads per row
-  const int64_t rows = (int64_t)nq * H;
-  const int64_t row = (int64_t)blockIdx.x * (256 / kPer) + threadIdx.x / kPer;
+preprocess_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                  const float* __restrict__ lse, int32_t nq, int32_t H,
+                  float* __restrict__ delta, float* __restrict__ lse2) {
+  constexpr int kPer = D / 16;          // threads per row
+  constexpr int kRows = 256 / kPer;     // rows per block
+  const int h = blockIdx.x % H;
+  const int i = (blockIdx.x / H) * kRows + threadIdx.x / kPer;
   const int part = threadIdx.x % kPer;
   float acc = 0.f;
-  if (row < rows) {
+  if (i < nq) {
     float a[16], b[16];
-    load16<T>(o + row * D + part * 16, a);
-    load16<T>(dout + row * D + part * 16, b);
+    const size_t off = ((size_t)i * H + h) * D + part * 16;
+    load16<T>(o + off, a);
+    load16<T>(dout + off, b);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc = fmaf(a[i], b[i], acc);
+    for (int e = 0; e < 16; ++e) acc = fmaf(a[e], b[e], acc);
   }
 #pragma unroll
-  for (int off = kPer / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) {
-    const int i = (int)(row / H), h = (int)(row % H);
+  for (int s = kPer / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
+  if (i < nq && part == 0) {
     delta[(size_t)h * nq + i] = acc;
+    const float l = lse[(size_t)h * nq + i];
+    lse2[(size_t)h * nq + i] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
 // ------------------------------------------------------------------ bf16 dq
-template <int D>
-struct DqBf16 {
-  static constexpr int kSub = 32;                 // key rows per inner step
-  static constexpr int kRow = D * 2 + 16;         // bytes per K / V row in LDS
-  static constexpr int kTRow = kSub * 2 + 8;      // bytes per K^T row in LDS
-  static constexpr int kK = 0;
-  static constexpr int kV = kK + kSub * kRow;
-  static constexpr int kKt = kV + kSub * kRow;
-  static constexpr int kId = kKt + D * kTRow;
-  static constexpr int kBuf = kId + kSub * 4;
-  static constexpr int kBlocks = (kSub / 4) * (D / 8);  // 4x8 blocks per operand
-  static constexpr int kDB = D / 32, kKK = D / 16;
-};
+constexpr int kTile64 = 64 * kRowBytes;
+constexpr int kDqStage = 2 * kTile64 + 256;  // K tile, V tile, 64 key ids
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-               const float* __restrict__ lse, const float* __restrict__ delta,
+               const float* __restrict__ delta, const float* __restrict__ lse2,
                const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
                int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
                const uint8_t* __restrict__ tile_class, const int32_t* __restrict__ q_ptr,
                const int32_t* __restrict__ q_cols, const int32_t* __restrict__ q_order,
                int32_t nkt, uint16_t* __restrict__ dq) {
-  using C = DqBf16<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBuf];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int kDB = D / 32, kKK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kDqStage];
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int work = blockIdx.x / H, h = blockIdx.x - work * H;
   const int qt = q_order[work];
   const int beg = q_ptr[qt];
-  const int nsub = 4 * (q_ptr[qt + 1] - beg);
+  const int nsub = 2 * (q_ptr[qt + 1] - beg);
   const size_t rs = (size_t)H * D;
+  const int hoff = h * D;
 
   const int qrow = qt * 128 + wv * 32 + col;
   const bool qin = qrow < nq;
   const int qc = qin ? qrow : nq - 1;
-  const int qtag = qin ? query_tag(q_ids[qrow]) : kPadQuery;
-  const float l_raw = lse[(size_t)h * nq + qc];
-  const float lse2 = l_raw == -INFINITY ? INFINITY : l_raw * kLog2e;  // P = 0 on empty rows
+  const int qid = qin ? q_ids[qrow] : -1;
+  const bool qvalid = qid >= 0;
+  const float nl2 = -lse2[(size_t)h * nq + qc];  // -inf on rows without a key: P = 0
   const float dlt = delta[(size_t)h * nq + qc];
 
-  bf16x8 qf[C::kKK], df[C::kKK];
+  bf16x8 qf[kKK], df[kKK];
   {
-    const uint16_t* qp = q + (size_t)qc * rs + h * D + 8 * hi;
-    const uint16_t* dp = dout + (size_t)qc * rs + h * D + 8 * hi;
+    const uint16_t* qp = q + (size_t)qc * rs + hoff + 8 * hi;
+    const uint16_t* dp = dout + (size_t)qc * rs + hoff + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < C::kKK; ++kk) {
+    for (int kk = 0; kk < kKK; ++kk) {
       qf[kk] = *(const bf16x8*)(qp + 16 * kk);
       df[kk] = *(const bf16x8*)(dp + 16 * kk);
     }
   }
-  f32x16 acc[C::kDB];
+  int toff[kDB][2];
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
+  for (int db = 0; db < kDB; ++db) {
+    toff[db][0] = tr_off(lane, db, 0);
+    toff[db][1] = tr_off(lane, db, 1);
+  }
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
 
-  if (nsub > 0) {
-    // threads 0..127 stage K (row-major and transposed), 128..255 stage V
-    const int b = tid & 127;
-    const bool is_v = tid >= 128;
-    const bool stager = b < C::kBlocks;
-    const int kg = b / (D / 8), dc = b % (D / 8);
-    u32x4 reg[4];
-    int32_t idreg = kPadKey;
-    auto gload = [&](int s) {
-      const int kt = q_cols[beg + (s >> 2)];
-      const int k0 = kt * 128 + (s & 3) * C::kSub;
-      if (stager) {
-        const uint16_t* src = is_v ? v : k;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kr = min(k0 + 4 * kg + r, nkv - 1);
-          reg[r] = *(const u32x4*)(src + (size_t)kr * rs + h * D + dc * 8);
-        }
-      }
-      if (tid < C::kSub) {
-        const int kr = k0 + tid;
-        idreg = kr < nkv ? key_tag(kv_ids[kr]) : kPadKey;
-      }
-    };
-    auto lstore = [&](int buf) {
-      char* base = smem + buf * C::kBuf;
-      if (stager) {
-        char* rm = base + (is_v ? C::kV : C::kK);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *(u32x4*)(rm + (4 * kg + r) * C::kRow + 16 * dc) = reg[r];
-        if (!is_v) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int w = c >> 1, sh = (c & 1) * 16;
-            const uint32_t x0 = (reg[0][w] >> sh) & 0xFFFFu, x1 = (reg[1][w] >> sh) & 0xFFFFu;
-            const uint32_t x2 = (reg[2][w] >> sh) & 0xFFFFu, x3 = (reg[3][w] >> sh) & 0xFFFFu;
-            u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-            *(u32x2*)(base + C::kKt + (8 * dc + c) * C::kTRow + 8 * kg) = pk;
-          }
-        }
-      }
-      if (tid < C::kSub) ((int32_t*)(base + C::kId))[tid] = idreg;
-    };
+  auto stage = [&](int s) {
+    const int kt = q_cols[beg + (s >> 1)];
+    const int k0 = kt * 128 + (s & 1) * 64;
+    char* base = smem + (s & 1) * kDqStage;
+    stage_tile<D, 64, 4>(k, rs, hoff, k0, nkv, base, wv, lane);
+    stage_tile<D, 64, 4>(v, rs, hoff, k0, nkv, base + kTile64, wv, lane);
+    if (wv == 0) stage_words(kv_ids, k0, nkv, base + 2 * kTile64, lane);
+  };
 
-    gload(0);
-    lstore(0);
+  if (nsub > 0) stage(0);
+  for (int s = 0; s < nsub; ++s) {
+    wait_vmem();
     __syncthreads();
-    for (int s = 0; s < nsub; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nsub) gload(s + 1);
-      const int kt = q_cols[beg + (s >> 2)];
-      const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-      const char* base = smem + buf * C::kBuf;
-
-      f32x16 st, dpt;  // S^T and dP^T: keys 8(j/4)+4hi+j%4 x query `col`
+    if (s + 1 < nsub) stage(s + 1);
+    const int kt = q_cols[beg + (s >> 1)];
+    const int k0 = kt * 128 + (s & 1) * 64;
+    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
+    const char* base = smem + (s & 1) * kDqStage;
+    const int32_t* il = (const int32_t*)(base + 2 * kTile64);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {  // 32 keys at a time
+      f32x16 st, dpt;  // S^T, dP^T: keys 32mb + 8(j/4) + 4hi + j%4 x query `col`
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[j] = dpt[j] = 0.f;
-      const char* krow = base + C::kK + col * C::kRow + 16 * hi;
-      const char* vrow = base + C::kV + col * C::kRow + 16 * hi;
 #pragma unroll
-      for (int kk = 0; kk < C::kKK; ++kk) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + 32 * kk), qf[kk],
-                                                      st, 0, 0, 0);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vrow + 32 * kk), df[kk],
-                                                       dpt, 0, 0, 0);
+      for (int kk = 0; kk < kKK; ++kk) {
+        const int ro = row_off(lane, kk) + 8192 * mb;
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(base, ro), qf[kk], st, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(base + kTile64, ro), df[kk], dpt,
+                                                       0, 0, 0);
       }
       float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(st[j] * s2 - lse2);
+      for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(st[j], s2, nl2));
       if (partial) {
-        const int32_t* il = (const int32_t*)(base + C::kId);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int4 t4 = *(const int4*)(il + 8 * g + 4 * hi);
-          if (t4.x != qtag) p[4 * g + 0] = 0.f;
-          if (t4.y != qtag) p[4 * g + 1] = 0.f;
-          if (t4.z != qtag) p[4 * g + 2] = 0.f;
-          if (t4.w != qtag) p[4 * g + 3] = 0.f;
+          const int r0 = mb * 32 + 8 * g + 4 * hi;
+          const int4 t4 = *(const int4*)(il + r0);
+          const int lim = nkv - k0 - r0;
+          p[4 * g + 0] = (qvalid & (t4.x == qid) & (lim > 0)) ? p[4 * g + 0] : 0.f;
+          p[4 * g + 1] = (qvalid & (t4.y == qid) & (lim > 1)) ? p[4 * g + 1] : 0.f;
+          p[4 * g + 2] = (qvalid & (t4.z == qid) & (lim > 2)) ? p[4 * g + 2] : 0.f;
+          p[4 * g + 3] = (qvalid & (t4.w == qid) & (lim > 3)) ? p[4 * g + 3] : 0.f;
         }
       }
-      bf16x8 ds[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         u32x4 w;
@@ -229,29 +201,21 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const int j = 8 * kb + 2 * e;
           w[e] = pack_bf16x2(p[j] * (dpt[j] - dlt), p[j + 1] * (dpt[j + 1] - dlt));
         }
-        ds[kb] = __builtin_bit_cast(bf16x8, w);
-      }
-      // dQ^T += K^T dS^T
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, w);
+        // dQ^T += K^T dS^T over keys 32mb + 16kb .. +15
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const char* kt_row = base + C::kKt + (db * 32 + col) * C::kTRow + 8 * hi;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x2 lo = *(const u32x2*)(kt_row + 32 * kb);
-          const u32x2 up = *(const u32x2*)(kt_row + 32 * kb + 16);
-          const u32x4 w = {lo[0], lo[1], up[0], up[1]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                            ds[kb], acc[db], 0, 0, 0);
+        for (int db = 0; db < kDB; ++db) {
+          const int o2 = 8192 * mb + 4096 * kb;
+          const bf16x8 a = join8(lds_tr4(base, toff[db][0] + o2), lds_tr4(base, toff[db][1] + o2));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb, acc[db], 0, 0, 0);
         }
       }
-      if (s + 1 < nsub) lstore(buf ^ 1);
-      __syncthreads();
     }
   }
   if (qin) {
-    uint16_t* op = dq + (size_t)qrow * rs + h * D;
+    uint16_t* op = dq + (size_t)qrow * rs + hoff;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 pk;
@@ -263,166 +227,111 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ------------------------------------------------------------------ bf16 dk, dv
-template <int D>
-struct DkvBf16 {
-  static constexpr int kSub = 32;             // query rows per inner step
-  static constexpr int kRow = D * 2 + 16;     // bytes per Q / dO row in LDS
-  static constexpr int kTRow = kSub * 2 + 8;  // bytes per Q^T / dO^T row in LDS
-  static constexpr int kQ = 0;
-  static constexpr int kDo = kQ + kSub * kRow;
-  static constexpr int kQt = kDo + kSub * kRow;
-  static constexpr int kDot = kQt + D * kTRow;
-  static constexpr int kLse = kDot + D * kTRow;
-  static constexpr int kDelta = kLse + kSub * 4;
-  static constexpr int kTag = kDelta + kSub * 4;
-  static constexpr int kBuf = kTag + kSub * 4;
-  static constexpr int kBlocks = (kSub / 4) * (D / 8);
-  static constexpr int kDB = D / 32, kKK = D / 16;
-};
+constexpr int kKvStage = 2 * kTile64 + 3 * 256;  // Q tile, dO tile, ids, lse2, delta
 
 template <int D>
 __global__ void __launch_bounds__(256)
 dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                 const float* __restrict__ lse, const float* __restrict__ delta,
+                 const float* __restrict__ delta, const float* __restrict__ lse2,
                  const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
                  int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
                  const uint8_t* __restrict__ tile_class, const int32_t* __restrict__ kv_ptr,
                  const int32_t* __restrict__ kv_rows, const int32_t* __restrict__ kv_order,
                  int32_t nkt, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using C = DkvBf16<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBuf];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int kDB = D / 32, kKK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kKvStage];
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int work = blockIdx.x / H, h = blockIdx.x - work * H;
   const int kt = kv_order[work];
   const int beg = kv_ptr[kt];
-  const int nsub = 4 * (kv_ptr[kt + 1] - beg);
+  const int nsub = 2 * (kv_ptr[kt + 1] - beg);
   const size_t rs = (size_t)H * D;
+  const int hoff = h * D;
 
   const int krow = kt * 128 + wv * 32 + col;
   const bool kin = krow < nkv;
   const int kc = kin ? krow : nkv - 1;
-  const int ktag = kin ? key_tag(kv_ids[krow]) : kPadKey;
+  const int kid = kin ? kv_ids[krow] : -1;
+  const bool kvalid = kid >= 0;
 
-  bf16x8 kf[C::kKK], vf[C::kKK];
+  bf16x8 kf[kKK], vf[kKK];
   {
-    const uint16_t* kp = k + (size_t)kc * rs + h * D + 8 * hi;
-    const uint16_t* vp = v + (size_t)kc * rs + h * D + 8 * hi;
+    const uint16_t* kp = k + (size_t)kc * rs + hoff + 8 * hi;
+    const uint16_t* vp = v + (size_t)kc * rs + hoff + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < C::kKK; ++kk) {
+    for (int kk = 0; kk < kKK; ++kk) {
       kf[kk] = *(const bf16x8*)(kp + 16 * kk);
       vf[kk] = *(const bf16x8*)(vp + 16 * kk);
     }
   }
-  f32x16 dka[C::kDB], dva[C::kDB];
+  int toff[kDB][2];
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
+  for (int db = 0; db < kDB; ++db) {
+    toff[db][0] = tr_off(lane, db, 0);
+    toff[db][1] = tr_off(lane, db, 1);
+  }
+  f32x16 dka[kDB], dva[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dka[db][j] = dva[db][j] = 0.f;
 
-  if (nsub > 0) {
-    // threads 0..127 stage Q, 128..255 stage dO (each row-major and transposed)
-    const int b = tid & 127;
-    const bool is_do = tid >= 128;
-    const bool stager = b < C::kBlocks;
-    const int qg = b / (D / 8), dc = b % (D / 8);
-    u32x4 reg[4];
-    float lreg = INFINITY, dreg = 0.f;
-    int32_t treg = kPadQuery;
-    auto gload = [&](int s) {
-      const int qt = kv_rows[beg + (s >> 2)];
-      const int q0 = qt * 128 + (s & 3) * C::kSub;
-      if (stager) {
-        const uint16_t* src = is_do ? dout : q;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qr = min(q0 + 4 * qg + r, nq - 1);
-          reg[r] = *(const u32x4*)(src + (size_t)qr * rs + h * D + dc * 8);
-        }
-      }
-      if (tid < C::kSub) {
-        const int qr = q0 + tid;
-        if (qr < nq) {
-          const float l = lse[(size_t)h * nq + qr];
-          lreg = l == -INFINITY ? INFINITY : l * kLog2e;
-          dreg = delta[(size_t)h * nq + qr];
-          treg = query_tag(q_ids[qr]);
-        } else {
-          lreg = INFINITY;
-          dreg = 0.f;
-          treg = kPadQuery;
-        }
-      }
-    };
-    auto lstore = [&](int buf) {
-      char* base = smem + buf * C::kBuf;
-      if (stager) {
-        char* rm = base + (is_do ? C::kDo : C::kQ);
-        char* tr = base + (is_do ? C::kDot : C::kQt);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *(u32x4*)(rm + (4 * qg + r) * C::kRow + 16 * dc) = reg[r];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int w = c >> 1, sh = (c & 1) * 16;
-          const uint32_t x0 = (reg[0][w] >> sh) & 0xFFFFu, x1 = (reg[1][w] >> sh) & 0xFFFFu;
-          const uint32_t x2 = (reg[2][w] >> sh) & 0xFFFFu, x3 = (reg[3][w] >> sh) & 0xFFFFu;
-          u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *(u32x2*)(tr + (8 * dc + c) * C::kTRow + 8 * qg) = pk;
-        }
-      }
-      if (tid < C::kSub) {
-        ((float*)(base + C::kLse))[tid] = lreg;
-        ((float*)(base + C::kDelta))[tid] = dreg;
-        ((int32_t*)(base + C::kTag))[tid] = treg;
-      }
-    };
+  auto stage = [&](int s) {
+    const int qt = kv_rows[beg + (s >> 1)];
+    const int q0 = qt * 128 + (s & 1) * 64;
+    char* base = smem + (s & 1) * kKvStage;
+    stage_tile<D, 64, 4>(q, rs, hoff, q0, nq, base, wv, lane);
+    stage_tile<D, 64, 4>(dout, rs, hoff, q0, nq, base + kTile64, wv, lane);
+    if (wv == 1) stage_words(q_ids, q0, nq, base + 2 * kTile64, lane);
+    if (wv == 2) stage_words(lse2 + (size_t)h * nq, q0, nq, base + 2 * kTile64 + 256, lane);
+    if (wv == 3) stage_words(delta + (size_t)h * nq, q0, nq, base + 2 * kTile64 + 512, lane);
+  };
 
-    gload(0);
-    lstore(0);
+  if (nsub > 0) stage(0);
+  for (int s = 0; s < nsub; ++s) {
+    wait_vmem();
     __syncthreads();
-    for (int s = 0; s < nsub; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nsub) gload(s + 1);
-      const int qt = kv_rows[beg + (s >> 2)];
-      const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-      const char* base = smem + buf * C::kBuf;
-
-      f32x16 sc, dpc;  // S and dP: queries 8(j/4)+4hi+j%4 x key `col`
+    if (s + 1 < nsub) stage(s + 1);
+    const int qt = kv_rows[beg + (s >> 1)];
+    const int q0 = qt * 128 + (s & 1) * 64;
+    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
+    const char* base = smem + (s & 1) * kKvStage;
+    const int32_t* qi = (const int32_t*)(base + 2 * kTile64);
+    const float* l2 = (const float*)(base + 2 * kTile64 + 256);
+    const float* dl = (const float*)(base + 2 * kTile64 + 512);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {  // 32 queries at a time
+      f32x16 sc, dpc;  // S, dP: queries 32mb + 8(j/4) + 4hi + j%4 x key `col`
 #pragma unroll
       for (int j = 0; j < 16; ++j) sc[j] = dpc[j] = 0.f;
-      const char* qrow = base + C::kQ + col * C::kRow + 16 * hi;
-      const char* drow = base + C::kDo + col * C::kRow + 16 * hi;
 #pragma unroll
-      for (int kk = 0; kk < C::kKK; ++kk) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qrow + 32 * kk), kf[kk],
-                                                      sc, 0, 0, 0);
-        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(drow + 32 * kk), vf[kk],
-                                                       dpc, 0, 0, 0);
+      for (int kk = 0; kk < kKK; ++kk) {
+        const int ro = row_off(lane, kk) + 8192 * mb;
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(base, ro), kf[kk], sc, 0, 0, 0);
+        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(base + kTile64, ro), vf[kk], dpc,
+                                                       0, 0, 0);
       }
-      const float* lsel = (const float*)(base + C::kLse);
-      const float* dlt = (const float*)(base + C::kDelta);
-      const int32_t* tg = (const int32_t*)(base + C::kTag);
-      float p[16], dl[16];
+      float p[16], dsv[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)(lsel + 8 * g + 4 * hi);
-        const f32x4 d4 = *(const f32x4*)(dlt + 8 * g + 4 * hi);
+        const int r0 = mb * 32 + 8 * g + 4 * hi;
+        const f32x4 l4 = *(const f32x4*)(l2 + r0);
+        const f32x4 d4 = *(const f32x4*)(dl + r0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * g + e;
-          p[j] = __builtin_amdgcn_exp2f(sc[j] * s2 - l4[e]);
-          dl[j] = d4[e];
-        }
+        for (int e = 0; e < 4; ++e) p[4 * g + e] = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + e], s2, -l4[e]));
         if (partial) {
-          const int4 t4 = *(const int4*)(tg + 8 * g + 4 * hi);
-          if (t4.x != ktag) p[4 * g + 0] = 0.f;
-          if (t4.y != ktag) p[4 * g + 1] = 0.f;
-          if (t4.z != ktag) p[4 * g + 2] = 0.f;
-          if (t4.w != ktag) p[4 * g + 3] = 0.f;
+          const int4 t4 = *(const int4*)(qi + r0);
+          const int lim = nq - q0 - r0;
+          p[4 * g + 0] = (kvalid & (t4.x == kid) & (lim > 0)) ? p[4 * g + 0] : 0.f;
+          p[4 * g + 1] = (kvalid & (t4.y == kid) & (lim > 1)) ? p[4 * g + 1] : 0.f;
+          p[4 * g + 2] = (kvalid & (t4.z == kid) & (lim > 2)) ? p[4 * g + 2] : 0.f;
+          p[4 * g + 3] = (kvalid & (t4.w == kid) & (lim > 3)) ? p[4 * g + 3] : 0.f;
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[4 * g + e] = p[4 * g + e] * (dpc[4 * g + e] - d4[e]);
       }
-      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         u32x4 wp, wd;
@@ -430,39 +339,28 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int e = 0; e < 4; ++e) {
           const int j = 8 * kb + 2 * e;
           wp[e] = pack_bf16x2(p[j], p[j + 1]);
-          wd[e] = pack_bf16x2(p[j] * (dpc[j] - dl[j]), p[j + 1] * (dpc[j + 1] - dl[j + 1]));
+          wd[e] = pack_bf16x2(dsv[j], dsv[j + 1]);
         }
-        pb[kb] = __builtin_bit_cast(bf16x8, wp);
-        dsb[kb] = __builtin_bit_cast(bf16x8, wd);
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, wp);
+        const bf16x8 db8 = __builtin_bit_cast(bf16x8, wd);
+        const int o2 = 8192 * mb + 4096 * kb;
+        // dV^T += dO^T P and dK^T += Q^T dS over queries 32mb + 16kb .. +15
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const char* dot_row = base + C::kDot + (db * 32 + col) * C::kTRow + 8 * hi;
-        const char* qt_row = base + C::kQt + (db * 32 + col) * C::kTRow + 8 * hi;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x2 a0 = *(const u32x2*)(dot_row + 32 * kb);
-          const u32x2 a1 = *(const u32x2*)(dot_row + 32 * kb + 16);
-          const u32x4 wa = {a0[0], a0[1], a1[0], a1[1]};
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wa),
-                                                            pb[kb], dva[db], 0, 0, 0);
-          const u32x2 b0 = *(const u32x2*)(qt_row + 32 * kb);
-          const u32x2 b1 = *(const u32x2*)(qt_row + 32 * kb + 16);
-          const u32x4 wb = {b0[0], b0[1], b1[0], b1[1]};
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wb),
-                                                            dsb[kb], dka[db], 0, 0, 0);
+        for (int db = 0; db < kDB; ++db) {
+          const bf16x8 ao = join8(lds_tr4(base + kTile64, toff[db][0] + o2),
+                                  lds_tr4(base + kTile64, toff[db][1] + o2));
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dva[db], 0, 0, 0);
+          const bf16x8 aq = join8(lds_tr4(base, toff[db][0] + o2), lds_tr4(base, toff[db][1] + o2));
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db8, dka[db], 0, 0, 0);
         }
       }
-      if (s + 1 < nsub) lstore(buf ^ 1);
-      __syncthreads();
     }
   }
   if (kin) {
-    uint16_t* kp = dk + (size_t)krow * rs + h * D;
-    uint16_t* vp = dv + (size_t)krow * rs + h * D;
+    uint16_t* kp = dk + (size_t)krow * rs + hoff;
+    uint16_t* vp = dv + (size_t)krow * rs + hoff;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 a, b;
@@ -619,67 +517,56 @@ dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 }
 
 template <typename T, int D>
-void launch_delta(const void* o, const void* dout, int32_t nq, int32_t H, float* delta,
-                  hipStream_t s) {
-  constexpr int kPer = D / 16;
-  const int64_t rows = (int64_t)nq * H;
-  const int64_t blocks = (rows + (256 / kPer) - 1) / (256 / kPer);
-  hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, (const T*)o,
-                     (const T*)dout, nq, H, delta);
+void launch_preprocess(const void* o, const void* dout, const float* lse, int32_t nq, int32_t H,
+                       float* delta, float* lse2, hipStream_t s) {
+  constexpr int kRows = 256 / (D / 16);
+  const int64_t blocks = (int64_t)((nq + kRows - 1) / kRows) * H;
+  hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const T*)o, (const T*)dout, lse, nq, H, delta, lse2);
 }
 
-}  // namespace
-
-extern "C" size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv,
-                                                  int32_t heads, int32_t head_dim) {
-  if ((dtype != PA_F32 && dtype != PA_BF16) || nq < 1 || nkv < 1 || heads < 1 ||
-      (head_dim != 64 && head_dim != 128))
-    return 0;
-  return pa::align_up((size_t)heads * nq * sizeof(float), 256);
-}
-
-namespace {
-
-// Launches one stage of the backward; stage 0 = Delta, 1 = dQ, 2 = dK/dV.
+// Launches one stage of the backward: 0 = preprocess, 1 = dQ, 2 = dK/dV.
+// `ws` holds Delta [H][nq] followed by LSE*log2(e) [H][nq].
 int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                   int32_t head_dim, float scale, const void* q, const void* k, const void* v,
                   const void* o, const void* dout, const float* lse, const int32_t* q_seq_id,
                   const int32_t* kv_seq_id, const pa_block_mask* mask, void* dq, void* dk,
-                  void* dv, float* delta, hipStream_t s) {
-  const dim3 gq(mask->nq_tiles * heads), gk(mask->nkv_tiles * heads);
+                  void* dv, float* ws, hipStream_t s) {
+  const dim3 gq(mask ? mask->nq_tiles * heads : 1), gk(mask ? mask->nkv_tiles * heads : 1);
   const float s2 = scale * pa::kLog2e;
   const bool bf = dtype == PA_BF16;
-  const dim3 bqd(mask->block_q), bkd(mask->block_kv);
+  float* delta = ws;
+  float* lse2 = ws + (size_t)heads * nq;
 #define PA_BWD_STAGES(D)                                                                         \
   if (stage == 0) {                                                                              \
-    if (bf) launch_delta<uint16_t, D>(o, dout, nq, heads, delta, s);                             \
-    else launch_delta<float, D>(o, dout, nq, heads, delta, s);                                   \
+    if (bf) launch_preprocess<uint16_t, D>(o, dout, lse, nq, heads, delta, lse2, s);             \
+    else launch_preprocess<float, D>(o, dout, lse, nq, heads, delta, lse2, s);                   \
   } else if (stage == 1) {                                                                       \
     if (bf)                                                                                      \
       hipLaunchKernelGGL(dq_bf16_kernel<D>, gq, dim3(256), 0, s, (const uint16_t*)q,             \
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,     \
-                         delta, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                  \
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
+                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
                          mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,             \
                          mask->nkv_tiles, (uint16_t*)dq);                                        \
     else                                                                                         \
-      hipLaunchKernelGGL(dq_f32_kernel<D>, gq, bqd, 0, s, (const float*)q, (const float*)k,      \
-                         (const float*)v, (const float*)dout, lse, delta, q_seq_id, kv_seq_id,   \
-                         nq, nkv, heads, scale, mask->block_q, mask->block_kv,                   \
-                         mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,             \
-                         mask->nkv_tiles, (float*)dq);                                           \
+      hipLaunchKernelGGL(dq_f32_kernel<D>, gq, dim3(mask->block_q), 0, s, (const float*)q,       \
+                         (const float*)k, (const float*)v, (const float*)dout, lse, delta,       \
+                         q_seq_id, kv_seq_id, nq, nkv, heads, scale, mask->block_q,              \
+                         mask->block_kv, mask->tile_class, mask->q_ptr, mask->q_cols,            \
+                         mask->q_order, mask->nkv_tiles, (float*)dq);                            \
   } else {                                                                                       \
     if (bf)                                                                                      \
       hipLaunchKernelGGL(dkdv_bf16_kernel<D>, gk, dim3(256), 0, s, (const uint16_t*)q,           \
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,     \
-                         delta, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                  \
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
+                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
                          mask->tile_class, mask->kv_ptr, mask->kv_rows, mask->kv_order,          \
                          mask->nkv_tiles, (uint16_t*)dk, (uint16_t*)dv);                         \
     else                                                                                         \
-      hipLaunchKernelGGL(dkdv_f32_kernel<D>, gk, bkd, 0, s, (const float*)q, (const float*)k,    \
-                         (const float*)v, (const float*)dout, lse, delta, q_seq_id, kv_seq_id,   \
-                         nq, nkv, heads, scale, mask->block_q, mask->block_kv,                   \
-                         mask->tile_class, mask->kv_ptr, mask->kv_rows, mask->kv_order,          \
-                         mask->nkv_tiles, (float*)dk, (float*)dv);                               \
+      hipLaunchKernelGGL(dkdv_f32_kernel<D>, gk, dim3(mask->block_kv), 0, s, (const float*)q,    \
+                         (const float*)k, (const float*)v, (const float*)dout, lse, delta,       \
+                         q_seq_id, kv_seq_id, nq, nkv, heads, scale, mask->block_q,              \
+                         mask->block_kv, mask->tile_class, mask->kv_ptr, mask->kv_rows,          \
+                         mask->kv_order, mask->nkv_tiles, (float*)dk, (float*)dv);               \
   }
   if (head_dim == 128) {
     PA_BWD_STAGES(128)
@@ -695,58 +582,76 @@ int32_t check_tensor(const void* p) {
   return pa::aligned16(p) ? PA_OK : PA_ERR_ALIGN;
 }
 
+size_t workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, int32_t head_dim) {
+  if ((dtype != PA_F32 && dtype != PA_BF16) || nq < 1 || nkv < 1 || heads < 1 ||
+      (head_dim != 64 && head_dim != 128))
+    return 0;
+  return pa::align_up(2 * (size_t)heads * nq * sizeof(float), 256);
+}
+
+int32_t check_workspace(const void* ws, size_t bytes, int32_t dtype, int32_t nq, int32_t heads,
+                        int32_t head_dim) {
+  if (!ws) return PA_ERR_NULL;
+  if (bytes < workspace_bytes(dtype, nq, 1, heads, head_dim)) return PA_ERR_WORKSPACE;
+  return pa::aligned256(ws) ? PA_OK : PA_ERR_ALIGN;
+}
+
 }  // namespace
+
+extern "C" size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv,
+                                                  int32_t heads, int32_t head_dim) {
+  return workspace_bytes(dtype, nq, nkv, heads, head_dim);
+}
 
 extern "C" int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t heads,
                                               int32_t head_dim, const void* o, const void* dout,
-                                              float* delta, void* stream) {
+                                              const float* lse, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_HEADDIM;
   if (nq < 1 || heads < 1) return PA_ERR_SHAPE;
-  if (!delta) return PA_ERR_NULL;
+  if (!lse) return PA_ERR_NULL;
+  int32_t st;
   for (const void* p : {o, dout})
-    if (int32_t st = check_tensor(p)) return st;
-  const hipStream_t s = (hipStream_t)stream;
-  if (head_dim == 128) {
-    if (dtype == PA_BF16) launch_delta<uint16_t, 128>(o, dout, nq, heads, delta, s);
-    else launch_delta<float, 128>(o, dout, nq, heads, delta, s);
-  } else {
-    if (dtype == PA_BF16) launch_delta<uint16_t, 64>(o, dout, nq, heads, delta, s);
-    else launch_delta<float, 64>(o, dout, nq, heads, delta, s);
-  }
-  return pa::launch_status();
+    if ((st = check_tensor(p))) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
+  return bwd_stage(0, dtype, nq, 1, heads, head_dim, 0.f, nullptr, nullptr, nullptr, o, dout,
+                   lse, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (float*)workspace,
+                   (hipStream_t)stream);
 }
 
 extern "C" int32_t attn_packed_bwd_dq(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                                       int32_t head_dim, float scale, const void* q, const void* k,
                                       const void* v, const void* dout, const float* lse,
-                                      const float* delta, const int32_t* q_seq_id,
-                                      const int32_t* kv_seq_id, const pa_block_mask* mask,
-                                      void* dq, void* stream) {
+                                      const void* workspace, size_t workspace_bytes,
+                                      const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                                      const pa_block_mask* mask, void* dq, void* stream) {
   int32_t st = pa::check_attn_args(dtype, nq, nkv, heads, head_dim, mask);
   if (st != PA_OK) return st;
-  if (!lse || !delta || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
+  if (!lse || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
   for (const void* p : {q, k, v, dout, (const void*)dq})
     if ((st = check_tensor(p))) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
   return bwd_stage(1, dtype, nq, nkv, heads, head_dim, scale, q, k, v, nullptr, dout, lse,
-                   q_seq_id, kv_seq_id, mask, dq, nullptr, nullptr, (float*)delta,
+                   q_seq_id, kv_seq_id, mask, dq, nullptr, nullptr, (float*)workspace,
                    (hipStream_t)stream);
 }
 
 extern "C" int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                                         int32_t head_dim, float scale, const void* q,
                                         const void* k, const void* v, const void* dout,
-                                        const float* lse, const float* delta,
-                                        const int32_t* q_seq_id, const int32_t* kv_seq_id,
-                                        const pa_block_mask* mask, void* dk, void* dv,
-                                        void* stream) {
+                                        const float* lse, const void* workspace,
+                                        size_t workspace_bytes, const int32_t* q_seq_id,
+                                        const int32_t* kv_seq_id, const pa_block_mask* mask,
+                                        void* dk, void* dv, void* stream) {
   int32_t st = pa::check_attn_args(dtype, nq, nkv, heads, head_dim, mask);
   if (st != PA_OK) return st;
-  if (!lse || !delta || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
+  if (!lse || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
   for (const void* p : {q, k, v, dout, (const void*)dk, (const void*)dv})
     if ((st = check_tensor(p))) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
   return bwd_stage(2, dtype, nq, nkv, heads, head_dim, scale, q, k, v, nullptr, dout, lse,
-                   q_seq_id, kv_seq_id, mask, nullptr, dk, dv, (float*)delta,
+                   q_seq_id, kv_seq_id, mask, nullptr, dk, dv, (float*)workspace,
                    (hipStream_t)stream);
 }
 
@@ -759,17 +664,14 @@ extern "C" int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32
                                    void* stream) {
   int32_t st = pa::check_attn_args(dtype, nq, nkv, heads, head_dim, mask);
   if (st != PA_OK) return st;
-  if (!lse || !q_seq_id || !kv_seq_id || !workspace) return PA_ERR_NULL;
+  if (!lse || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
   for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if ((st = check_tensor(p))) return st;
-  if (workspace_bytes < attn_packed_bwd_workspace_bytes(dtype, nq, nkv, heads, head_dim))
-    return PA_ERR_WORKSPACE;
-  if (!pa::aligned256(workspace)) return PA_ERR_ALIGN;
-  float* delta = (float*)workspace;
+  if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
   const hipStream_t s = (hipStream_t)stream;
   for (int stage = 0; stage < 3; ++stage) {
     st = bwd_stage(stage, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse,
-                   q_seq_id, kv_seq_id, mask, dq, dk, dv, delta, s);
+                   q_seq_id, kv_seq_id, mask, dq, dk, dv, (float*)workspace, s);
     if (st != PA_OK) return st;
   }
   return PA_OK;

@@ -63,11 +63,11 @@ def _load() -> ctypes.CDLL:
         "attn_packed_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "attn_packed_bwd": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   pm, vp, vp, vp, vp, sz, vp]),
-        "attn_packed_bwd_preprocess": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
-        "attn_packed_bwd_dq": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, pm, vp, vp]),
-        "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, pm, vp, vp, vp]),
+        "attn_packed_bwd_preprocess": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "attn_packed_bwd_dq": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
+                                     vp, vp, pm, vp, vp]),
+        "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
+                                       vp, vp, pm, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -260,57 +260,63 @@ def attn_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     return dq, dk, dv
 
 
-def attn_packed_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor,
-                               delta: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Delta ``[H, nq]`` float32 = row sums of ``dout * o``."""
+def attn_packed_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fill the backward workspace (row sums of ``dout * o`` and the LSE in log2 units)."""
     _need(o, "o")
     _need(dout, "dout", o.dtype, o.device)
+    _need(lse, "lse", torch.float32, o.device)
     if o.dtype not in _DTYPES or o.dim() != 3 or dout.shape != o.shape:
         raise ValueError("o and dout must be matching [nq, H, d] float32/bfloat16 tensors")
     nq, H, d = o.shape
-    if delta is None:
-        delta = torch.empty((H, nq), dtype=torch.float32, device=o.device)
-    _need(delta, "delta", torch.float32, o.device)
+    if tuple(lse.shape) != (H, nq):
+        raise ValueError("lse must be [H, nq]")
+    nbytes = attn_packed_bwd_workspace_bytes(o.dtype, nq, 1, H, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=o.device)
+    _need(workspace, "workspace", torch.uint8, o.device)
     _check(_lib.attn_packed_bwd_preprocess(_DTYPES[o.dtype], nq, H, d, o.data_ptr(),
-                                           dout.data_ptr(), delta.data_ptr(), _stream(o)),
+                                           dout.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel(), _stream(o)),
            "attn_packed_bwd_preprocess")
-    return delta
+    return workspace
 
 
-def attn_packed_bwd_dq(q, k, v, dout, lse, delta, q_seq_id, kv_seq_id, mask: BlockMask,
-                       scale: Optional[float] = None, dq: Optional[torch.Tensor] = None):
+def _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale):
     nq, nkv, H, d = _attn_shapes(q, k, v)
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, name, q.dtype, q.device)
     _need(lse, "lse", torch.float32, q.device)
-    _need(delta, "delta", torch.float32, q.device)
+    _need(workspace, "workspace", torch.uint8, q.device)
+    _need(q_seq_id, "q_seq_id", torch.int32, q.device)
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    return nq, nkv, H, d, float(scale)
+
+
+def attn_packed_bwd_dq(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mask: BlockMask,
+                       scale: Optional[float] = None, dq: Optional[torch.Tensor] = None):
+    nq, nkv, H, d, scale = _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale)
     dq = torch.empty_like(q) if dq is None else dq
-    _check(_lib.attn_packed_bwd_dq(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
+    _check(_lib.attn_packed_bwd_dq(_DTYPES[q.dtype], nq, nkv, H, d, scale, q.data_ptr(),
                                    k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                                   delta.data_ptr(), q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
-                                   ctypes.byref(mask.desc), dq.data_ptr(), _stream(q)),
-           "attn_packed_bwd_dq")
+                                   workspace.data_ptr(), workspace.numel(), q_seq_id.data_ptr(),
+                                   kv_seq_id.data_ptr(), ctypes.byref(mask.desc), dq.data_ptr(),
+                                   _stream(q)), "attn_packed_bwd_dq")
     return dq
 
 
-def attn_packed_bwd_dkdv(q, k, v, dout, lse, delta, q_seq_id, kv_seq_id, mask: BlockMask,
+def attn_packed_bwd_dkdv(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mask: BlockMask,
                          scale: Optional[float] = None, dk: Optional[torch.Tensor] = None,
                          dv: Optional[torch.Tensor] = None):
-    nq, nkv, H, d = _attn_shapes(q, k, v)
-    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _need(t, name, q.dtype, q.device)
-    _need(lse, "lse", torch.float32, q.device)
-    _need(delta, "delta", torch.float32, q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+    nq, nkv, H, d, scale = _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _check(_lib.attn_packed_bwd_dkdv(_DTYPES[q.dtype], nq, nkv, H, d, float(scale),
-                                     q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                     lse.data_ptr(), delta.data_ptr(), q_seq_id.data_ptr(),
-                                     kv_seq_id.data_ptr(), ctypes.byref(mask.desc),
-                                     dk.data_ptr(), dv.data_ptr(), _stream(q)),
-           "attn_packed_bwd_dkdv")
+    _check(_lib.attn_packed_bwd_dkdv(_DTYPES[q.dtype], nq, nkv, H, d, scale, q.data_ptr(),
+                                     k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(),
+                                     q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
+                                     ctypes.byref(mask.desc), dk.data_ptr(), dv.data_ptr(),
+                                     _stream(q)), "attn_packed_bwd_dkdv")
     return dk, dv
