@@ -71,14 +71,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
   }
-  int koff[kKK], voff[kDB][2];
-#pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) koff[kk] = row_off(lane, kk);
-#pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    voff[db][0] = kFwdTile + tr_off(lane, db, 0);
-    voff[db][1] = kFwdTile + tr_off(lane, db, 1);
-  }
+  const int rb = row_base(lane), tb = tr_base(lane);
 
   f32x16 oacc[kDB];
 #pragma unroll
@@ -116,7 +109,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk)
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_row8(base, koff[kk] + 8192 * mb), qf[kk], sacc[mb], 0, 0, 0);
+            lds_row8(base, row_at(rb, kk) + 8192 * mb), qf[kk], sacc[mb], 0, 0, 0);
     }
     if (partial) {
       const int32_t* il = (const int32_t*)(base + 2 * kFwdTile);
@@ -176,8 +169,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = join8(lds_tr4(base, voff[db][0] + 4096 * kb),
-                               lds_tr4(base, voff[db][1] + 4096 * kb));
+        const bf16x8 a = join8(lds_tr4(base + kFwdTile, tr_at(tb, db, 0) + 4096 * kb),
+                               lds_tr4(base + kFwdTile, tr_at(tb, db, 1) + 4096 * kb));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], oacc[db], 0, 0, 0);
       }
   }

@@ -109,4 +109,17 @@ __device__ __forceinline__ int tr_off(int lane, int db, int s) {
   return row * kRowBytes + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
 }
 
+// Lane-constant bases of the same offsets.  Both offset families only differ
+// per instruction in bits that the base keeps free or XORs, so
+//   row_off(lane, kk)   == row_base(lane) ^ (32 * kk)
+//   tr_off(lane, db, s) == (tr_base(lane) ^ (64 * db + 32 * s)) + 2048 * s
+// (the row swizzle term of 16*chunk XORs into bits 4..7; rows sit in bits >= 8).
+// One v_xor per offset keeps only two address registers live.
+__device__ __forceinline__ int row_base(int lane) { return row_off(lane, 0); }
+__device__ __forceinline__ int tr_base(int lane) { return tr_off(lane, 0, 0); }
+__device__ __forceinline__ int row_at(int base, int kk) { return base ^ (32 * kk); }
+__device__ __forceinline__ int tr_at(int base, int db, int s) {
+  return (base ^ (64 * db + 32 * s)) + 2048 * s;
+}
+
 }  // namespace pa

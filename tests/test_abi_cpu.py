@@ -135,3 +135,38 @@ def test_mask_shape_hazard_is_rejected(lib):
     assert lib.attn_packed_bwd(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                FAKE, FAKE, ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, ws - 1,
                                None) == PA_ERR_WORKSPACE
+
+
+def test_tile_offset_identities():
+    """The XOR forms of the LDS operand offsets equal the direct formulas
+    (host re-implementation of the swizzle arithmetic in pa_tile.h)."""
+    def swz(r):
+        return ((r & 3) << 2) | ((r >> 2) & 3)
+
+    def row_off(lane, kk):
+        r = lane & 31
+        return r * 256 + (((2 * kk + (lane >> 5)) ^ swz(r)) << 4)
+
+    def tr_off(lane, db, s):
+        L, h, gm = lane & 15, lane >> 5, (lane >> 4) & 1
+        row = 4 * h + (L >> 2) + 8 * s
+        col = 32 * db + 16 * gm + 4 * (L & 3)
+        return row * 256 + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1)
+
+    for lane in range(64):
+        for kk in range(8):
+            assert row_off(lane, kk) == row_off(lane, 0) ^ (32 * kk)
+        for db in range(4):
+            for s in range(2):
+                assert tr_off(lane, db, s) == (tr_off(lane, 0, 0) ^ (64 * db + 32 * s)) + 2048 * s
+    # conflict-freedom of the two read patterns (16-byte bank groups of a 256-byte row)
+    for kk in range(8):
+        for g16 in range(4):
+            lanes = [16 * g16 + i for i in range(16)]
+            assert len({(row_off(l, kk) % 256) // 16 for l in lanes}) == 16
+    for db in range(4):
+        for s in range(2):
+            for half in range(2):
+                lanes = range(32 * half, 32 * half + 32)
+                banks = {(tr_off(l, db, s) % 1024) // 8 for l in lanes}
+                assert len(banks) == 32  # 32 distinct 8-byte slots within 4 rows
