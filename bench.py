@@ -28,8 +28,45 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 FLOPS_PER_PAIR = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
 
 
+KERNEL_SOURCES = {  # the files a kernel's code comes from (hashed to validate traffic figures)
+    "fwd": ["packed_variable_length_amd/csrc/attn_fwd.hip"],
+    "bwd_dq": ["packed_variable_length_amd/csrc/attn_bwd.hip"],
+    "bwd_dkdv": ["packed_variable_length_amd/csrc/attn_bwd.hip"],
+}
+COMMON_SOURCES = ["packed_variable_length_amd/csrc/pa_tile.h",
+                  "packed_variable_length_amd/csrc/pa_common.h"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha256(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[stage] + COMMON_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this kernel and workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_hbm.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha256(stage):
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(spec, q, k, v, do, heads):
@@ -162,9 +199,11 @@ def main():
                                             "bwd_dq": "dq_bf16_kernel<128>",
                                             "bwd_dkdv": "dkdv_bf16_kernel<128>"}[dom],
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, spec.name),
                 "flops_per_launch": FLOPS_PER_PAIR[dom] * d * pairs * H,
-                "avg_launch_ms": round(kernels[dom], 4)}
+                "avg_launch_ms": round(kernels[dom], 4),
+                "source_sha256": source_sha256(dom)}
 
     cpu = None
     if not args.no_cpu_baseline:
