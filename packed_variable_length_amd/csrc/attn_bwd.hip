@@ -16,8 +16,9 @@
 //   dq          query-major, one 128-row query tile per workgroup: S^T = K Q^T,
 //               dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (query index on the lanes)
 //   dkdv        key-major, one 128-row key tile per workgroup: S = Q K^T,
-//               dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS (key index on
-//               the lanes, dK and dV accumulated in registers)
+//               P (packed to bf16 at once), dP = dO V^T, dS from the bf16 P,
+//               dV^T += dO^T P, dK^T += Q^T dS (key index on the lanes, dK and
+//               dV accumulated in registers; sized to fit two waves per SIMD)
 // Splitting dQ from dK/dV recomputes S and dP once more (14 instead of 10
 // d*pairs flops per head) but needs no fp32 atomics, no zero-filled accumulator
 // and no conversion pass, and is deterministic.
@@ -225,7 +226,7 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 constexpr int kKvStage = 2 * kTile64 + 3 * 256;  // Q tile, dO tile, ids, lse2, delta
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                  const float* __restrict__ delta, const float* __restrict__ lse2,
@@ -291,38 +292,26 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int32_t* qi = (const int32_t*)(base + 2 * kTile64);
     const float* l2 = (const float*)(base + 2 * kTile64 + 256);
     const float* dl = (const float*)(base + 2 * kTile64 + 512);
-    // Software pipeline over the two 32-query halves (mb) of the stage: the
-    // S/dP products of half 1 are issued between the softmax-gradient VALU work
-    // of half 0, and the dV/dK products of half 0 between that of half 1, so the
-    // matrix core and the VALU run concurrently within the wave.
-    bf16x8 ra[kKK], rd[kKK];  // Q and dO row operands of one half
-    auto rows = [&](int mb) {
+    int rbi = rb, tbi = tb;
+    asm volatile("" : "+v"(rbi), "+v"(tbi));  // recompute operand offsets here, not hoisted
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) {
-        const int ro = row_at(rb, kk) + 8192 * mb;
-        ra[kk] = lds_row8(base, ro);
-        rd[kk] = lds_row8(base + kTile64, ro);
-      }
-    };
-    auto sdp = [&](f32x16& sc, f32x16& dpc) {
+    for (int mb = 0; mb < 2; ++mb) {  // 32 queries at a time
+      // S, then P packed to bf16 at once (frees S); then dP and dS from the bf16 P
+      f32x16 acc;  // queries 32mb + 8(j/4) + 4hi + j%4 x key `col`
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sc[j] = dpc[j] = 0.f;
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kk], kf[kk], sc, 0, 0, 0);
-        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd[kk], vf[kk], dpc, 0, 0, 0);
-      }
-    };
-    // P and dS of half mb as bf16 B operands (slots of query block kb)
-    auto grad = [&](int mb, const f32x16& sc, const f32x16& dpc, bf16x8* pb, bf16x8* dsb) {
+      for (int kk = 0; kk < kKK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(base, row_at(rbi, kk) + 8192 * mb),
+                                                      kf[kk], acc, 0, 0, 0);
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = mb * 32 + 8 * g + 4 * hi;
         const f32x4 l4 = *(const f32x4*)(l2 + r0);
-        const f32x4 d4 = *(const f32x4*)(dl + r0);
-        float p[4], ds[4];
+        float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + e], s2, -l4[e]));
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(acc[4 * g + e], s2, -l4[e]));
         if (partial) {
           const int4 t4 = *(const int4*)(qi + r0);
           const int lim = nq - q0 - r0;
@@ -331,59 +320,46 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           p[2] = (kvalid & (t4.z == kid) & (lim > 2)) ? p[2] : 0.f;
           p[3] = (kvalid & (t4.w == kid) & (lim > 3)) ? p[3] : 0.f;
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dpc[4 * g + e] - d4[e]);
         u32x4 wp = __builtin_bit_cast(u32x4, pb[g >> 1]);
-        u32x4 wd = __builtin_bit_cast(u32x4, dsb[g >> 1]);
         const int w0 = (g & 1) * 2;
         wp[w0] = pack_bf16x2(p[0], p[1]);
         wp[w0 + 1] = pack_bf16x2(p[2], p[3]);
-        wd[w0] = pack_bf16x2(ds[0], ds[1]);
-        wd[w0 + 1] = pack_bf16x2(ds[2], ds[3]);
         pb[g >> 1] = __builtin_bit_cast(bf16x8, wp);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            lds_row8(base + kTile64, row_at(rbi, kk) + 8192 * mb), vf[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = mb * 32 + 8 * g + 4 * hi;
+        const f32x4 d4 = *(const f32x4*)(dl + r0);
+        const u32x4 wp = __builtin_bit_cast(u32x4, pb[g >> 1]);
+        const int w0 = (g & 1) * 2;
+        const float p0 = bf16_bits_to_f32(wp[w0] & 0xFFFFu), p1 = bf16_bits_to_f32(wp[w0] >> 16);
+        const float p2 = bf16_bits_to_f32(wp[w0 + 1] & 0xFFFFu), p3 = bf16_bits_to_f32(wp[w0 + 1] >> 16);
+        u32x4 wd = __builtin_bit_cast(u32x4, dsb[g >> 1]);
+        wd[w0] = pack_bf16x2(p0 * (acc[4 * g] - d4[0]), p1 * (acc[4 * g + 1] - d4[1]));
+        wd[w0 + 1] = pack_bf16x2(p2 * (acc[4 * g + 2] - d4[2]), p3 * (acc[4 * g + 3] - d4[3]));
         dsb[g >> 1] = __builtin_bit_cast(bf16x8, wd);
       }
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS over queries 32mb + 16kb .. +15
-    auto dvdk = [&](int mb, const bf16x8* pb, const bf16x8* dsb) {
+      // dV^T += dO^T P and dK^T += Q^T dS over queries 32mb + 16kb .. +15
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int o2 = 8192 * mb + 4096 * kb;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          const bf16x8 ao = join8(lds_tr4(base + kTile64, tr_at(tb, db, 0) + o2),
-                                  lds_tr4(base + kTile64, tr_at(tb, db, 1) + o2));
-          const bf16x8 aq = join8(lds_tr4(base, tr_at(tb, db, 0) + o2),
-                                  lds_tr4(base, tr_at(tb, db, 1) + o2));
+          const bf16x8 ao = join8(lds_tr4(base + kTile64, tr_at(tbi, db, 0) + o2),
+                                  lds_tr4(base + kTile64, tr_at(tbi, db, 1) + o2));
           dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[kb], dva[db], 0, 0, 0);
+          const bf16x8 aq = join8(lds_tr4(base, tr_at(tbi, db, 0) + o2),
+                                  lds_tr4(base, tr_at(tbi, db, 1) + o2));
           dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[kb], dka[db], 0, 0, 0);
         }
       }
-    };
-    f32x16 sc0, dp0, sc1, dp1;
-    bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
-    rows(0);
-    sdp(sc0, dp0);
-    rows(1);
-    __builtin_amdgcn_sched_barrier(0);
-    sdp(sc1, dp1);
-    grad(0, sc0, dp0, pb0, ds0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {  // interleave: one MFMA, then VALU work
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    dvdk(0, pb0, ds0);
-    grad(1, sc1, dp1, pb1, ds1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    dvdk(1, pb1, ds1);
   }
   if (kin) {
     uint16_t* kp = dk + (size_t)krow * rs + hoff;

@@ -44,15 +44,31 @@ template <int D, int NROWS, int NW>
 __device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ g, size_t rs, int hoff,
                                            int row0, int n, char* tile, int wv, int lane) {
   static_assert(NROWS % 4 == 0, "tile rows come in groups of 4");
-  const int p = lane & 15;
+  const int p = lane & 15, rl = lane >> 4;  // physical chunk, row within the 4-row group
+  if (row0 + NROWS <= n) {
+    // Every row exists: a wave-uniform row base plus a per-lane byte offset
+    // (row r = 4*blk + rl has swz(r) = 4*rl + blk%4).
 #pragma unroll
-  for (int blk = wv; blk < NROWS / 4; blk += NW) {
-    const int r = blk * 4 + (lane >> 4);
-    int c = p ^ swz(r);
-    if (D == 64) c &= 7;  // 64-wide rows use chunks 0..7; other slots get a spare copy
-    const int gr = min(row0 + r, n - 1);
-    const uint16_t* src = g + (size_t)gr * rs + hoff + c * 8;
-    __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(tile + blk * 1024), 16, 0, 0);
+    for (int blk = wv; blk < NROWS / 4; blk += NW) {
+      int c = p ^ (4 * rl + (blk & 3));
+      if (D == 64) c &= 7;  // 64-wide rows use chunks 0..7; other slots get a spare copy
+      const uint32_t lane_off = (uint32_t)(((size_t)rl * rs + hoff + c * 8) * 2);
+      const char* base = (const char*)(g + (size_t)(row0 + 4 * blk) * rs);
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(base + lane_off),
+                                       (lds_void*)(tile + blk * 1024), 16, 0, 0);
+    }
+  } else {
+    // Tail tile: rows at or past n re-read row n - 1 (callers mask them).
+#pragma unroll
+    for (int blk = wv; blk < NROWS / 4; blk += NW) {
+      const int r = blk * 4 + rl;
+      int c = p ^ swz(r);
+      if (D == 64) c &= 7;
+      const int gr = min(row0 + r, n - 1);
+      const uint16_t* src = g + (size_t)gr * rs + hoff + c * 8;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(tile + blk * 1024), 16, 0,
+                                       0);
+    }
   }
 }
 
