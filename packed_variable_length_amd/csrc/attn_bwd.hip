@@ -108,7 +108,8 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const int32_t* __restrict__ q_cols, const int32_t* __restrict__ q_order,
                int32_t nkt, uint16_t* __restrict__ dq) {
   constexpr int kDB = D / 32, kKK = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kDqStage];
+  __shared__ __attribute__((aligned(1024))) char st0[kDqStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kDqStage];
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int work = blockIdx.x / H, h = blockIdx.x - work * H;
@@ -143,24 +144,24 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
 
-  auto stage = [&](int s) {
+  auto stage = [&](int s, char* base) {
     const int kt = q_cols[beg + (s >> 1)];
     const int k0 = kt * 128 + (s & 1) * 64;
-    char* base = smem + (s & 1) * kDqStage;
     stage_tile<D, 64, 4>(k, rs, hoff, k0, nkv, base, wv, lane);
     stage_tile<D, 64, 4>(v, rs, hoff, k0, nkv, base + kTile64, wv, lane);
-    if (wv == 0) stage_words(kv_ids, k0, nkv, base + 2 * kTile64, lane);
+    if (wv == 0) stage_ids(kv_ids, k0, nkv, base + 2 * kTile64, lane);
   };
 
-  if (nsub > 0) stage(0);
-  for (int s = 0; s < nsub; ++s) {
+  if (nsub > 0) stage(0, st0);
+  // Two LDS stage arrays and a loop unrolled by two: each step reads one
+  // array while the next stage's direct loads fill the other, so the
+  // compiler can see that its LDS reads never wait for those loads.
+  auto step = [&](int s, const char* base, char* next) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
-    if (s + 1 < nsub) stage(s + 1);
+    if (s + 1 < nsub) stage(s + 1, next);
     const int kt = q_cols[beg + (s >> 1)];
-    const int k0 = kt * 128 + (s & 1) * 64;
-    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-    const char* base = smem + (s & 1) * kDqStage;
+    const bool partial = tile_class_at(tile_class, (size_t)qt * nkt + kt) == 1;
     const int32_t* il = (const int32_t*)(base + 2 * kTile64);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {  // 32 keys at a time
@@ -181,12 +182,11 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = mb * 32 + 8 * g + 4 * hi;
-          const int4 t4 = *(const int4*)(il + r0);
-          const int lim = nkv - k0 - r0;
-          p[4 * g + 0] = (qvalid & (t4.x == qid) & (lim > 0)) ? p[4 * g + 0] : 0.f;
-          p[4 * g + 1] = (qvalid & (t4.y == qid) & (lim > 1)) ? p[4 * g + 1] : 0.f;
-          p[4 * g + 2] = (qvalid & (t4.z == qid) & (lim > 2)) ? p[4 * g + 2] : 0.f;
-          p[4 * g + 3] = (qvalid & (t4.w == qid) & (lim > 3)) ? p[4 * g + 3] : 0.f;
+          const int4 t4 = *(const int4*)(il + r0);  // -1 past the end of the keys
+          p[4 * g + 0] = (qvalid & (t4.x == qid)) ? p[4 * g + 0] : 0.f;
+          p[4 * g + 1] = (qvalid & (t4.y == qid)) ? p[4 * g + 1] : 0.f;
+          p[4 * g + 2] = (qvalid & (t4.z == qid)) ? p[4 * g + 2] : 0.f;
+          p[4 * g + 3] = (qvalid & (t4.w == qid)) ? p[4 * g + 3] : 0.f;
         }
       }
 #pragma unroll
@@ -207,6 +207,10 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       }
     }
+    };
+  for (int s = 0; s < nsub; s += 2) {
+    step(s, st0, st1);
+    if (s + 1 < nsub) step(s + 1, st1, st0);
   }
   if (qin) {
     uint16_t* op = dq + (size_t)qrow * rs + hoff;
@@ -236,7 +240,8 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ kv_rows, const int32_t* __restrict__ kv_order,
                  int32_t nkt, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   constexpr int kDB = D / 32, kKK = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kKvStage];
+  __shared__ __attribute__((aligned(1024))) char st0[kKvStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kKvStage];
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int work = blockIdx.x / H, h = blockIdx.x - work * H;
@@ -269,26 +274,26 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < 16; ++j) dka[db][j] = dva[db][j] = 0.f;
 
-  auto stage = [&](int s) {
+  auto stage = [&](int s, char* base) {
     const int qt = kv_rows[beg + (s >> 1)];
     const int q0 = qt * 128 + (s & 1) * 64;
-    char* base = smem + (s & 1) * kKvStage;
     stage_tile<D, 64, 4>(q, rs, hoff, q0, nq, base, wv, lane);
     stage_tile<D, 64, 4>(dout, rs, hoff, q0, nq, base + kTile64, wv, lane);
-    if (wv == 1) stage_words(q_ids, q0, nq, base + 2 * kTile64, lane);
+    if (wv == 1) stage_ids(q_ids, q0, nq, base + 2 * kTile64, lane);
     if (wv == 2) stage_words(lse2 + (size_t)h * nq, q0, nq, base + 2 * kTile64 + 256, lane);
     if (wv == 3) stage_words(delta + (size_t)h * nq, q0, nq, base + 2 * kTile64 + 512, lane);
   };
 
-  if (nsub > 0) stage(0);
-  for (int s = 0; s < nsub; ++s) {
+  if (nsub > 0) stage(0, st0);
+  // Two LDS stage arrays and a loop unrolled by two: each step reads one
+  // array while the next stage's direct loads fill the other, so the
+  // compiler can see that its LDS reads never wait for those loads.
+  auto step = [&](int s, const char* base, char* next) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
-    if (s + 1 < nsub) stage(s + 1);
+    if (s + 1 < nsub) stage(s + 1, next);
     const int qt = kv_rows[beg + (s >> 1)];
-    const int q0 = qt * 128 + (s & 1) * 64;
-    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-    const char* base = smem + (s & 1) * kKvStage;
+    const bool partial = tile_class_at(tile_class, (size_t)qt * nkt + kt) == 1;
     const int32_t* qi = (const int32_t*)(base + 2 * kTile64);
     const float* l2 = (const float*)(base + 2 * kTile64 + 256);
     const float* dl = (const float*)(base + 2 * kTile64 + 512);
@@ -313,12 +318,11 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(acc[4 * g + e], s2, -l4[e]));
         if (partial) {
-          const int4 t4 = *(const int4*)(qi + r0);
-          const int lim = nq - q0 - r0;
-          p[0] = (kvalid & (t4.x == kid) & (lim > 0)) ? p[0] : 0.f;
-          p[1] = (kvalid & (t4.y == kid) & (lim > 1)) ? p[1] : 0.f;
-          p[2] = (kvalid & (t4.z == kid) & (lim > 2)) ? p[2] : 0.f;
-          p[3] = (kvalid & (t4.w == kid) & (lim > 3)) ? p[3] : 0.f;
+          const int4 t4 = *(const int4*)(qi + r0);  // -1 past the end of the queries
+          p[0] = (kvalid & (t4.x == kid)) ? p[0] : 0.f;
+          p[1] = (kvalid & (t4.y == kid)) ? p[1] : 0.f;
+          p[2] = (kvalid & (t4.z == kid)) ? p[2] : 0.f;
+          p[3] = (kvalid & (t4.w == kid)) ? p[3] : 0.f;
         }
         u32x4 wp = __builtin_bit_cast(u32x4, pb[g >> 1]);
         const int w0 = (g & 1) * 2;
@@ -360,6 +364,10 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       }
     }
+    };
+  for (int s = 0; s < nsub; s += 2) {
+    step(s, st0, st1);
+    if (s + 1 < nsub) step(s + 1, st1, st0);
   }
   if (kin) {
     uint16_t* kp = dk + (size_t)krow * rs + hoff;

@@ -49,7 +49,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const int32_t* __restrict__ q_order, int32_t nkt, uint16_t* __restrict__ o,
                 float* __restrict__ lse) {
   constexpr int kDB = D / 32, kKK = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kFwdStage];
+  __shared__ __attribute__((aligned(1024))) char st0[kFwdStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kFwdStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
@@ -80,37 +81,43 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  auto stage = [&](int s) {
+  auto stage = [&](int s, char* base) {
     const int kt = q_cols[beg + (s >> 1)];
     const int k0 = kt * 128 + (s & 1) * kFwdSub;
-    char* base = smem + (s & 1) * kFwdStage;
     stage_tile<D, kFwdSub, 4>(k, rs, hoff, k0, nkv, base, wv, lane);
     stage_tile<D, kFwdSub, 4>(v, rs, hoff, k0, nkv, base + kFwdTile, wv, lane);
-    if (wv == 0) stage_words(kv_ids, k0, nkv, base + 2 * kFwdTile, lane);
+    if (wv == 0) stage_ids(kv_ids, k0, nkv, base + 2 * kFwdTile, lane);
   };
 
-  if (nsub > 0) stage(0);
-  for (int s = 0; s < nsub; ++s) {
+  if (nsub > 0) stage(0, st0);
+  // Two LDS stage arrays and a loop unrolled by two: each step reads one
+  // array while the next stage's direct loads fill the other, so the
+  // compiler can see that its LDS reads never wait for those loads.
+  auto step = [&](int s, const char* base, char* next) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();  // stage s is in LDS; every wave is done with stage s - 1
-    if (s + 1 < nsub) stage(s + 1);
+    if (s + 1 < nsub) stage(s + 1, next);
     const int kt = q_cols[beg + (s >> 1)];
-    const int k0 = kt * 128 + (s & 1) * kFwdSub;
-    const bool partial = tile_class[(size_t)qt * nkt + kt] == 1;
-    const char* base = smem + (s & 1) * kFwdStage;
+    const bool partial = tile_class_at(tile_class, (size_t)qt * nkt + kt) == 1;
 
     // S^T = K Q^T: 64 keys (two 32-key blocks) x this wave's 32 queries; lane
     // holds keys 32mb + 8(j/4) + 4hi + j%4 of query `col`
+    // K operands of the first key block are all requested before the first
+    // MFMA; each slot is refilled for the second block right after its use.
     f32x16 sacc[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int j = 0; j < 16; ++j) sacc[0][j] = sacc[1][j] = 0.f;
+    bf16x8 ka[kKK];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[mb][j] = 0.f;
+    for (int kk = 0; kk < kKK; ++kk) ka[kk] = lds_row8(base, row_at(rb, kk));
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk)
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_row8(base, row_at(rb, kk) + 8192 * mb), qf[kk], sacc[mb], 0, 0, 0);
+    for (int kk = 0; kk < kKK; ++kk) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], sacc[0], 0, 0, 0);
+      ka[kk] = lds_row8(base, row_at(rb, kk) + 8192);
     }
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk)
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], sacc[1], 0, 0, 0);
     if (partial) {
       const int32_t* il = (const int32_t*)(base + 2 * kFwdTile);
 #pragma unroll
@@ -118,13 +125,12 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = mb * 32 + 8 * g + 4 * hi;
-          const int4 t4 = *(const int4*)(il + r0);
-          const int lim = nkv - k0 - r0;  // keys r0 + e with e >= lim are past the end
-          // branch-free: bitwise & of the three conditions, then a select
-          const bool ok0 = qvalid & (t4.x == qid) & (lim > 0);
-          const bool ok1 = qvalid & (t4.y == qid) & (lim > 1);
-          const bool ok2 = qvalid & (t4.z == qid) & (lim > 2);
-          const bool ok3 = qvalid & (t4.w == qid) & (lim > 3);
+          const int4 t4 = *(const int4*)(il + r0);  // -1 past the end of the keys
+          // branch-free: bitwise & of the conditions, then a select
+          const bool ok0 = qvalid & (t4.x == qid);
+          const bool ok1 = qvalid & (t4.y == qid);
+          const bool ok2 = qvalid & (t4.z == qid);
+          const bool ok3 = qvalid & (t4.w == qid);
           sacc[mb][4 * g + 0] = ok0 ? sacc[mb][4 * g + 0] : -INFINITY;
           sacc[mb][4 * g + 1] = ok1 ? sacc[mb][4 * g + 1] : -INFINITY;
           sacc[mb][4 * g + 2] = ok2 ? sacc[mb][4 * g + 2] : -INFINITY;
@@ -173,6 +179,10 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                lds_tr4(base + kFwdTile, tr_at(tb, db, 1) + 4096 * kb));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], oacc[db], 0, 0, 0);
       }
+    };
+  for (int s = 0; s < nsub; s += 2) {
+    step(s, st0, st1);
+    if (s + 1 < nsub) step(s + 1, st1, st0);
   }
 
   // epilogue: both half-waves hold partial sums of the same query

@@ -81,6 +81,28 @@ __device__ __forceinline__ void stage_words(const void* __restrict__ src, int i0
                                    0, 0);
 }
 
+// A seq id no allowed pair carries (allowed pairs have ids >= 0); read, never written.
+__device__ int32_t kNoId = -1;
+
+// Copy the 64 seq ids ids[i0 .. i0+63] into LDS; positions at or past n get -1,
+// so a tail tile needs no separate bounds test (one wave instruction).
+__device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int i0, int n,
+                                          char* dst, int lane) {
+  const int i = i0 + lane;
+  const int32_t* src = i < n ? ids + i : &kNoId;
+  __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Class byte of tile pair `idx`, fetched as the aligned 32-bit word that holds
+// it: a uniform word address becomes a scalar (SMEM) load, which -- unlike a
+// vector byte load -- does not make the wave wait behind its outstanding
+// direct-to-LDS loads of the next stage.  The class array is padded to a
+// multiple of 256 bytes, so the word never leaves the allocation.
+__device__ __forceinline__ int tile_class_at(const uint8_t* __restrict__ cls, size_t idx) {
+  const uint32_t w = ((const uint32_t*)cls)[idx >> 2];
+  return (int)((w >> (8 * (idx & 3))) & 0xFFu);
+}
+
 // Wait for this wave's outstanding direct-to-LDS loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
