@@ -54,7 +54,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
-  const int work = blockIdx.x / H, h = blockIdx.x - work * H;
+  int work, h;
+  block_work(blockIdx.x, H, (nq + 127) / 128, &work, &h);
   const int qt = q_order[work];
   const int beg = q_ptr[qt];
   const int nsub = 2 * (q_ptr[qt + 1] - beg);

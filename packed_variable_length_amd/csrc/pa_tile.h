@@ -32,6 +32,23 @@ __device__ __forceinline__ int tile_byte(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }
 
+// Block -> (work item, head).  Workgroups are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8).  When the head count is a multiple of 8, XCD x
+// walks its heads x, x+8, ... one after the other, each over all work items in
+// the given (longest-first) order, so the blocks in flight on an XCD share one
+// head's K/V (or Q/dO) rows in that XCD's L2.  Otherwise heads vary fastest.
+__device__ __forceinline__ void block_work(int b, int H, int nwork, int* work, int* h) {
+  if ((H & 7) == 0) {
+    const int xcd = b & 7, slot = b >> 3;
+    const int hg = slot / nwork;
+    *work = slot - hg * nwork;
+    *h = xcd + 8 * hg;
+  } else {
+    *work = b / H;
+    *h = b - *work * H;
+  }
+}
+
 // Wave-uniform index of the calling wave inside its workgroup (kept in an SGPR).
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
