@@ -198,6 +198,49 @@ int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                              const int32_t* q_seq_id, const int32_t* kv_seq_id,
                              const pa_block_mask* mask, void* dk, void* dv, void* stream);
 
+/*
+ * Frame-valid masked squared-error loss ("LingBot-VA packing" report, section
+ * 2.1, compute_loss: on a padded pack the latent and action losses are averaged
+ * over valid frames only).  A token is valid iff its seq id is >= 0:
+ *   L = sum over valid rows i and channels c of (pred[i][c] - target[i][c])^2,
+ *       divided by (n_valid * C);  L = 0 when no row is valid;
+ *   dL/dpred = 2 (pred - target) / (n_valid * C) on valid rows, exact 0 on
+ *       padding rows.
+ * Sums run in fp32 in a fixed order: results are bitwise reproducible.
+ *
+ *   dtype        PA_F32 or PA_BF16 (pred, target and dpred share it)
+ *   n, C         rows (tokens) >= 0 and channels, C a multiple of 8, n*C <= 2^36;
+ *                n = 0 reads nothing (pred, target, seq_id, dpred may be NULL)
+ *                and gives stats {0, 0, 0, 0}
+ *   pred, target device [n][C], 16-byte aligned
+ *   seq_id       device int32[n]
+ *   stats        device fp32[4], written: {loss, sum of squared errors over
+ *                valid rows, n_valid (exact below 2^24), 2/(n_valid*C) or 0}
+ *   upstream     dL_total/dL, multiplies the gradient (1 for a plain loss)
+ *   dpred        device [n][C] of dtype, written (all rows), 16-byte aligned
+ *   workspace    device buffer of >= masked_mse_workspace_bytes(n) bytes (8 KiB
+ *                for any n; 0 means n < 0), 256-byte aligned, overwritten
+ * masked_mse_fwd      loss only: writes stats.
+ * masked_mse_bwd      gradient only, from the stats of a finished
+ *                     masked_mse_fwd on the same inputs (stats[3] is read);
+ *                     the same bits as masked_mse_fwd_bwd's dpred.
+ * masked_mse_fwd_bwd  both in one pass over pred and target (counts the valid
+ *                     rows from the ids first); writes stats and dpred.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIGN,
+ *         PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+size_t masked_mse_workspace_bytes(int32_t n);
+int32_t masked_mse_fwd(int32_t dtype, int32_t n, int32_t C, const void* pred, const void* target,
+                       const int32_t* seq_id, float* stats, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int32_t masked_mse_bwd(int32_t dtype, int32_t n, int32_t C, const void* pred, const void* target,
+                       const int32_t* seq_id, const float* stats, float upstream, void* dpred,
+                       void* stream);
+int32_t masked_mse_fwd_bwd(int32_t dtype, int32_t n, int32_t C, const void* pred,
+                           const void* target, const int32_t* seq_id, float upstream,
+                           float* stats, void* dpred, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,10 @@ from .packattn import (  # noqa: F401
     attn_packed_fwd,
     build_block_mask,
     build_block_mask_bytes,
+    masked_mse_bwd,
+    masked_mse_fwd,
+    masked_mse_fwd_bwd,
+    masked_mse_workspace_bytes,
     pa_status_str,
     seq_ids_from_valid_frames,
 )

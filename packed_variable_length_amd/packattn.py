@@ -68,6 +68,10 @@ def _load() -> ctypes.CDLL:
                                      vp, vp, pm, vp, vp]),
         "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
                                        vp, vp, pm, vp, vp, vp]),
+        "masked_mse_workspace_bytes": (sz, [i32]),
+        "masked_mse_fwd": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
+        "masked_mse_fwd_bwd": (i32, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -320,3 +324,70 @@ def attn_packed_bwd_dkdv(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mas
                                      ctypes.byref(mask.desc), dk.data_ptr(), dv.data_ptr(),
                                      _stream(q)), "attn_packed_bwd_dkdv")
     return dk, dv
+
+
+# ----------------------------------------------------------------- masked loss
+def masked_mse_workspace_bytes(n: int) -> int:
+    return int(_lib.masked_mse_workspace_bytes(int(n)))
+
+
+def _loss_args(pred, target, seq_id, workspace):
+    _need(pred, "pred")
+    if pred.dtype not in _DTYPES or pred.dim() != 2:
+        raise ValueError("pred must be a [n, C] float32/bfloat16 tensor")
+    _need(target, "target", pred.dtype, pred.device)
+    _need(seq_id, "seq_id", torch.int32, pred.device)
+    n, c = pred.shape
+    if target.shape != pred.shape or seq_id.numel() != n:
+        raise ValueError("target must match pred and seq_id must have one id per row")
+    if workspace is None:
+        workspace = torch.empty(max(masked_mse_workspace_bytes(n), 1), dtype=torch.uint8,
+                                device=pred.device)
+    _need(workspace, "workspace", torch.uint8, pred.device)
+    return n, c, workspace
+
+
+def masked_mse_fwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.Tensor,
+                   stats: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 ``stats[4]`` = (loss, sum of squared errors, n_valid, 2/(n_valid*C))."""
+    n, c, workspace = _loss_args(pred, target, seq_id, workspace)
+    stats = torch.empty(4, dtype=torch.float32, device=pred.device) if stats is None else stats
+    _need(stats, "stats", torch.float32, pred.device)
+    _check(_lib.masked_mse_fwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
+                               seq_id.data_ptr(), stats.data_ptr(), workspace.data_ptr(),
+                               workspace.numel(), _stream(pred)), "masked_mse_fwd")
+    return stats
+
+
+def masked_mse_bwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.Tensor,
+                   stats: torch.Tensor, upstream: float = 1.0,
+                   dpred: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the loss w.r.t. ``pred`` (times ``upstream``), from forward ``stats``."""
+    n, c, _ = _loss_args(pred, target, seq_id, torch.empty(1, dtype=torch.uint8,
+                                                            device=pred.device))
+    _need(stats, "stats", torch.float32, pred.device)
+    dpred = torch.empty_like(pred) if dpred is None else dpred
+    _need(dpred, "dpred", pred.dtype, pred.device)
+    _check(_lib.masked_mse_bwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
+                               seq_id.data_ptr(), stats.data_ptr(), float(upstream),
+                               dpred.data_ptr(), _stream(pred)), "masked_mse_bwd")
+    return dpred
+
+
+def masked_mse_fwd_bwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.Tensor,
+                       upstream: float = 1.0, stats: Optional[torch.Tensor] = None,
+                       dpred: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Loss stats and gradient in one pass over ``pred`` and ``target``."""
+    n, c, workspace = _loss_args(pred, target, seq_id, workspace)
+    stats = torch.empty(4, dtype=torch.float32, device=pred.device) if stats is None else stats
+    dpred = torch.empty_like(pred) if dpred is None else dpred
+    _need(stats, "stats", torch.float32, pred.device)
+    _need(dpred, "dpred", pred.dtype, pred.device)
+    _check(_lib.masked_mse_fwd_bwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
+                                   seq_id.data_ptr(), float(upstream), stats.data_ptr(),
+                                   dpred.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream(pred)), "masked_mse_fwd_bwd")
+    return stats, dpred

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("seq_ids_from_valid_frames", "build_block_mask", "build_block_mask_bytes",
                  "attn_packed_fwd", "attn_packed_bwd", "attn_packed_bwd_workspace_bytes",
-                 "pa_status_str"):
+                 "pa_status_str", "masked_mse_fwd", "masked_mse_bwd", "masked_mse_fwd_bwd",
+                 "masked_mse_workspace_bytes"):
         assert want in names
 
 
@@ -170,3 +171,27 @@ def test_tile_offset_identities():
                 lanes = range(32 * half, 32 * half + 32)
                 banks = {(tr_off(l, db, s) % 1024) // 8 for l in lanes}
                 assert len(banks) == 32  # 32 distinct 8-byte slots within 4 rows
+
+
+def test_masked_loss_argument_errors(lib):
+    ws = lib.masked_mse_workspace_bytes(1000)
+    assert ws >= 8192 and lib.masked_mse_workspace_bytes(-1) == 0
+    f = lambda **kw: lib.masked_mse_fwd(kw.get("dt", 1), kw.get("n", 1000), kw.get("c", 192),  # noqa: E731
+                                        kw.get("p", FAKE), FAKE, kw.get("ids", FAKE), FAKE,
+                                        kw.get("ws", FAKE), kw.get("nb", ws), None)
+    assert f(dt=3) == PA_ERR_DTYPE
+    assert f(c=100) == PA_ERR_SHAPE            # C must be a multiple of 8
+    assert f(n=-1) == PA_ERR_SHAPE
+    assert f(n=1 << 30, c=1 << 10) == PA_ERR_SHAPE
+    assert f(ids=None) == PA_ERR_NULL
+    assert f(p=ctypes.c_void_p(0x100008)) == PA_ERR_ALIGN
+    assert f(nb=ws - 1) == PA_ERR_WORKSPACE
+    assert f(ws=ctypes.c_void_p(0x100010)) == PA_ERR_ALIGN
+    assert lib.masked_mse_bwd(1, 1000, 192, FAKE, FAKE, FAKE, None, 1.0, FAKE, None) == PA_ERR_NULL
+    assert lib.masked_mse_bwd(1, 1000, 192, FAKE, FAKE, FAKE, FAKE, 1.0,
+                              ctypes.c_void_p(0x100004), None) == PA_ERR_ALIGN
+    assert lib.masked_mse_bwd(1, 0, 192, None, None, None, None, 1.0, None, None) == PA_OK
+    assert lib.masked_mse_fwd_bwd(1, 1000, 192, FAKE, FAKE, FAKE, 1.0, FAKE, None, FAKE, ws,
+                                  None) == PA_ERR_NULL
+    assert lib.masked_mse_fwd_bwd(1, 1000, 192, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, 16,
+                                  None) == PA_ERR_WORKSPACE

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for packed segment-id attention.
 
 This package only draws inputs: episode lengths, padded frame counts, per-token
-segment ids given directly (long mixed-modality pack), and the random q, k, v,
-dO values.  It holds none of the attention arithmetic and none of the seq-id or
+segment ids given directly (long mixed-modality pack), the random q, k, v,
+dO values and the random predictions/targets of the masked loss.  It holds none of the attention arithmetic and none of the seq-id or
 block-mask construction, so both the CPU oracle and the HIP path can be fed
 from it without sharing any of the method's code.
 """
@@ -13,4 +13,5 @@ from .packs import (  # noqa: F401
     bucketed_sweep,
     round_to_bf16,
     make_values,
+    make_loss_values,
 )

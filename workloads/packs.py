@@ -27,6 +27,7 @@ __all__ = [
     "bucketed_sweep",
     "round_to_bf16",
     "make_values",
+    "make_loss_values",
 ]
 
 
@@ -109,6 +110,21 @@ def make_values(spec: PackSpec):
         if spec.dtype == "bf16":
             a = round_to_bf16(a)
         out.append(a)
+    return tuple(out)
+
+
+def make_loss_values(n: int, channels: int, dtype: str, seed):
+    """Draw a prediction and its target as float32 arrays ``[n, channels]``.
+
+    Both ~ N(0, 1) from ``np.random.default_rng(seed)`` (prediction first);
+    bf16 is rounded to bf16 (RNE).  Stand-ins for the latent (video) and
+    action regression outputs whose loss is masked to valid frames.
+    """
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(2):
+        a = rng.standard_normal((int(n), int(channels)), dtype=np.float32)
+        out.append(round_to_bf16(a) if dtype == "bf16" else a)
     return tuple(out)
 
 
