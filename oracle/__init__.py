@@ -15,10 +15,13 @@ Pages cited (by title and section):
     seq id of -1 removes a token from attention as both query and key, and
     tokens only attend to tokens with the same seq id.
   * "LingBot-VA attention profiling" report -- next steps: the document-id
-    mask predicate ``doc_id[q] == doc_id[k]``.
+    mask predicate ``doc_id[q] == doc_id[k]``; conclusion: several episodes
+    concatenated per GPU up to its token budget.
 
 Modules:
-  seqids     -- per-token seq ids from valid frames
+  seqids     -- per-token seq ids from valid frames or from episode lengths
+  packing    -- next-fit assignment of episodes to packs under a token budget
+  loss       -- frame-valid masked squared-error loss and its gradient
   blockmask  -- per tile-pair valid-pair counts, classes and CSR lists
   attention  -- per-episode dense softmax attention and its gradients
 
@@ -26,4 +29,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against brute
 force, torch's fp64 attention with autograd, finite differences, closed forms
 and the pages' invariants; none is marked "parity unpinned".
 """
-from . import seqids, blockmask, attention  # noqa: F401
+from . import seqids, blockmask, attention, loss, packing  # noqa: F401

@@ -27,3 +27,24 @@ def seq_ids_from_valid_frames(valid_frames, frames_padded: int, tokens_per_frame
             tag = b if f < vf else -1
             out.extend([tag] * int(tokens_per_frame))
     return np.asarray(out, dtype=np.int32)
+
+
+def seq_ids_from_lengths(lengths, n_tokens: int) -> np.ndarray:
+    """Seq ids of an unpadded pack: episodes concatenated back to back.
+
+    "LingBot-VA attention profiling" report, next steps: the collate step
+    concatenates K episodes along the sequence axis and gives every token its
+    document id (here the episode's position in ``lengths``).  The id buffer
+    has a fixed length ``n_tokens``: positions past the last episode are
+    padding (-1); an episode that runs past ``n_tokens`` is cut there.  A
+    negative length counts as 0.
+    """
+    out = np.full(int(n_tokens), -1, dtype=np.int32)
+    pos = 0
+    for e, n in enumerate(list(lengths)):
+        for _ in range(max(int(n), 0)):
+            if pos >= n_tokens:
+                return out
+            out[pos] = e
+            pos += 1
+    return out

@@ -338,3 +338,67 @@ def test_useful_pairs_closed_form():
     # sum over episodes of (32 * frames)^2
     assert oatt.useful_pairs(ids, ids) == sum((32 * int(f)) ** 2 for f in (119, 177, 285, 239))
     assert oatt.useful_pairs(ids, ids) == 188248064
+
+
+# ----------------------------------------------------------------- unpadded packing
+def _read_unpadded_fixture(path):
+    cases = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kind, rest = line.split(None, 1) if " " in line else (line, "")
+        a, b, c = (x.strip() for x in rest.split("|"))
+        lengths = [int(x) for x in a.split(",")] if a else []
+        if kind == "ids":
+            cases.append(("ids", lengths, int(b), [int(x) for x in c.split(",")]))
+        else:
+            cases.append(("packs", lengths, int(b),
+                          [[int(x) for x in p.split(",")] for p in c.split(";")]))
+    return cases
+
+
+def test_unpadded_hand_worked_fixture(golden_dir):
+    from oracle import packing as opk
+    cases = _read_unpadded_fixture(os.path.join(golden_dir, "unpadded_packs_small.txt"))
+    assert len(cases) == 7
+    for kind, lengths, n, want in cases:
+        if kind == "ids":
+            assert osid.seq_ids_from_lengths(lengths, n).tolist() == want, (lengths, n)
+        else:
+            assert opk.next_fit_packs(lengths, n) == want, (lengths, n)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_unpadded_ids_equal_repeat_construction(seed):
+    """Same ids as numpy's repeat of the episode index, cut / padded to length."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(-3, 40, int(rng.integers(0, 12)))
+    n = int(rng.integers(1, 300))
+    rep = np.repeat(np.arange(len(lengths), dtype=np.int32), np.maximum(lengths, 0))
+    want = np.full(n, -1, np.int32)
+    want[:min(n, len(rep))] = rep[:n]
+    assert np.array_equal(osid.seq_ids_from_lengths(lengths, n), want)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_next_fit_is_the_unique_order_preserving_maximal_partition(seed):
+    """Next-fit is characterised by: packs are consecutive runs of the input
+    order, each within the budget, and each pack's first episode would not
+    have fit in the pack before it.  Check those three properties."""
+    from oracle import packing as opk
+    rng = np.random.default_rng(seed)
+    budget = int(rng.integers(5, 60))
+    lengths = rng.integers(0, budget + 1, int(rng.integers(1, 40))).tolist()
+    packs = opk.next_fit_packs(lengths, budget)
+    assert [e for p in packs for e in p] == list(range(len(lengths)))
+    sums = [sum(lengths[e] for e in p) for p in packs]
+    assert all(s <= budget for s in sums) and all(len(p) > 0 for p in packs)
+    for k in range(1, len(packs)):
+        assert sums[k - 1] + lengths[packs[k][0]] > budget
+
+
+def test_next_fit_rejects_an_episode_over_budget():
+    from oracle import packing as opk
+    with pytest.raises(ValueError):
+        opk.next_fit_packs([3, 11, 2], 10)
