@@ -134,6 +134,50 @@ def bench_masked_loss(pa, ids, channels=192, iters=50):
             "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
 
 
+def bench_unpadded_pack(pa, iters=5):
+    """Whole hot path (ids from lengths, mask, fwd, bwd) on the first 68,000-token
+    unpadded pack the next-fit packer makes from the episode stream."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    lengths = wl.episode_stream()
+    pack_of, _ = pa.plan_token_packs(lengths, wl.UNPADDED_BUDGET)
+    sel = lengths[pack_of == 0]
+    s = wl.unpadded_pack(sel)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    mk = lambda: (0.5 * torch.randn((s.nq, s.heads, s.head_dim), generator=g,  # noqa: E731
+                                    device=dev)).to(torch.bfloat16)
+    Q, K, V = mk(), mk(), mk()
+    DO = (2 * mk().float()).to(torch.bfloat16)
+    L = torch.from_numpy(sel).to(dev)
+    ids = torch.empty(s.nq, dtype=torch.int32, device=dev)
+    O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+    lse = torch.empty((s.heads, s.nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(pa.attn_packed_bwd_workspace_bytes(torch.bfloat16, s.nq, s.nq, s.heads,
+                                                        s.head_dim), dtype=torch.uint8,
+                     device=dev)
+    mstore = torch.empty(pa.build_block_mask_bytes(s.nq, s.nq, 128, 128), dtype=torch.uint8,
+                         device=dev)
+
+    def step():
+        pa.seq_ids_from_lengths(L, s.nq, out=ids)
+        mask = pa.build_block_mask(ids, ids, 128, 128, storage=mstore)
+        pa.attn_packed_fwd(Q, K, V, ids, ids, mask, s.scale, out=O, lse=lse)
+        pa.attn_packed_bwd(Q, K, V, O, DO, lse, ids, ids, mask, s.scale, workspace=ws,
+                           grads=(dQ, dK, dV))
+    ms = time_calls(step, iters, warmup=2)
+    pairs = int((sel.astype(np.int64) ** 2).sum())
+    useful = 14.0 * s.head_dim * pairs * s.heads
+    tf = useful / (ms * 1e-3) / 1e12
+    return {"workload": f"{len(sel)} episodes ({int(sel.sum())} tokens) back to back in a "
+                        f"{s.nq}-token buffer, {s.heads} heads x {s.head_dim} bf16",
+            "ms_per_step": round(ms, 4), "useful_TFLOPs": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "tokens_per_s": round(int(sel.sum()) / (ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,9 +290,11 @@ def main():
                 "source_sha256": source_sha256(dom)}
 
     extras = {"masked_loss": bench_masked_loss(pa, ids)}
-    for name, r in extras.items():
-        log(f"[bench] {name}: {r['avg_call_ms'] * 1e3:.1f} us, {r['achieved_GBs']} GB/s "
-            f"({100 * r['frac']:.1f}% of HBM peak)")
+    r = extras["masked_loss"]
+    log(f"[bench] masked_loss: {r['avg_call_ms'] * 1e3:.1f} us, {r['achieved_GBs']} GB/s "
+        f"({100 * r['frac']:.1f}% of HBM peak)")
+    extras["unpadded_pack"] = r = bench_unpadded_pack(pa)
+    log(f"[bench] unpadded pack: {r['ms_per_step']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -70,6 +70,37 @@ int32_t seq_ids_from_valid_frames(const int32_t* valid_frames, int32_t B, int32_
                                   int32_t tokens_per_frame, int32_t* seq_id, void* stream);
 
 /*
+ * Unpadded packing ("LingBot-VA attention profiling" report, conclusion and
+ * next steps: concatenate several episodes along the sequence axis, each token
+ * tagged with its document id; "LingBot-VA packing" report, section 1: fill
+ * the per-GPU token budget of about 68k tokens).
+ *
+ * plan_token_packs -- HOST function: assigns episodes, in the given order, to
+ *   packs of at most `budget` tokens, next-fit (a pack is closed when the next
+ *   episode would overflow it; that episode opens the next pack).
+ *     lengths  host int32[B], tokens per episode, each in [0, budget]
+ *     pack_of  host int32[B], written: pack index of each episode (0, 1, ...)
+ *     n_packs  host int32, written: number of packs (0 when B = 0)
+ *   Errors: PA_ERR_SHAPE (B < 0, budget < 1, a length outside [0, budget]),
+ *           PA_ERR_NULL.
+ *
+ * seq_ids_from_lengths -- ids of one unpadded pack: episode e (0-based, in
+ *   order) takes the next max(lengths[e], 0) tokens and gives them id e;
+ *   positions past the last episode get -1; tokens past n_tokens are cut.
+ *     lengths   device int32[B], B in [0, 8192]
+ *     n_tokens  length of the id buffer (a fixed shape; >= 0)
+ *     seq_id    device int32[n_tokens], written
+ *     offsets   device int32[B + 1] or NULL; if given, written with each
+ *               episode's first token (clamped to n_tokens) and, last, the
+ *               number of tokens that carry an id
+ *   Errors: PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_HIP.
+ */
+int32_t plan_token_packs(const int32_t* lengths, int32_t B, int64_t budget, int32_t* pack_of,
+                         int32_t* n_packs);
+int32_t seq_ids_from_lengths(const int32_t* lengths, int32_t B, int32_t n_tokens,
+                             int32_t* seq_id, int32_t* offsets, void* stream);
+
+/*
  * Block mask: the per-tile sparsity of the same-id predicate
  * ("LingBot-VA packing" report, sections 1 and 2.2: a block mask built from the
  * seq ids; blocks without an allowed pair are skipped).

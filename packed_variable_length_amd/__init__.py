@@ -22,5 +22,7 @@ from .packattn import (  # noqa: F401
     masked_mse_fwd_bwd,
     masked_mse_workspace_bytes,
     pa_status_str,
+    plan_token_packs,
+    seq_ids_from_lengths,
     seq_ids_from_valid_frames,
 )

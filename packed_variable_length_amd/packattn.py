@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
                                      vp, vp, pm, vp, vp]),
         "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
                                        vp, vp, pm, vp, vp, vp]),
+        "plan_token_packs": (i32, [vp, i32, ctypes.c_int64, vp, vp]),
+        "seq_ids_from_lengths": (i32, [vp, i32, i32, vp, vp, vp]),
         "masked_mse_workspace_bytes": (sz, [i32]),
         "masked_mse_fwd": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
@@ -324,6 +326,39 @@ def attn_packed_bwd_dkdv(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mas
                                      ctypes.byref(mask.desc), dk.data_ptr(), dv.data_ptr(),
                                      _stream(q)), "attn_packed_bwd_dkdv")
     return dk, dv
+
+
+# ------------------------------------------------------------ unpadded packing
+def plan_token_packs(lengths, budget: int):
+    """Host next-fit plan: returns (pack index per episode as an int32 numpy
+    array, number of packs)."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    pack_of = np.empty(len(arr), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(_lib.plan_token_packs(arr.ctypes.data if len(arr) else None, len(arr), int(budget),
+                                 pack_of.ctypes.data if len(arr) else None, ctypes.byref(n)),
+           "plan_token_packs")
+    return pack_of, int(n.value)
+
+
+def seq_ids_from_lengths(lengths: torch.Tensor, n_tokens: int,
+                         out: Optional[torch.Tensor] = None, offsets: bool = False):
+    """int32 ids ``[n_tokens]`` of an unpadded pack (and the episode offsets
+    ``[B + 1]`` when ``offsets`` is true)."""
+    _need(lengths, "lengths", torch.int32)
+    B = lengths.numel()
+    if out is None:
+        out = torch.empty(int(n_tokens), dtype=torch.int32, device=lengths.device)
+    _need(out, "out", torch.int32, lengths.device)
+    if out.numel() != int(n_tokens):
+        raise ValueError(f"out has {out.numel()} elements, expected {n_tokens}")
+    off = torch.empty(B + 1, dtype=torch.int32, device=lengths.device) if offsets else None
+    _check(_lib.seq_ids_from_lengths(lengths.data_ptr() if B else None, B, int(n_tokens),
+                                     out.data_ptr() if n_tokens else None,
+                                     off.data_ptr() if off is not None else None,
+                                     _stream(lengths)), "seq_ids_from_lengths")
+    return (out, off) if offsets else out
 
 
 # ----------------------------------------------------------------- masked loss

@@ -17,8 +17,8 @@ PA_ERR_MASK_MISMATCH, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_ALIGN = -5, -6, -7, -
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from packed_variable_length_amd import build as b  # noqa: WPS433 (build on demand)
-        b.build(verbose=False)
+        import __graft_entry__  # build on demand (loads build.py by path)
+        __graft_entry__._build_module().build(verbose=False)
     from packed_variable_length_amd import packattn  # loads the library, checks signatures
     return packattn._lib
 

@@ -1,10 +1,11 @@
 """Seeded synthetic inputs for packed segment-id attention.
 
 This package only draws inputs: episode lengths, padded frame counts, per-token
-segment ids given directly (long mixed-modality pack), the random q, k, v,
-dO values and the random predictions/targets of the masked loss.  It holds none of the attention arithmetic and none of the seq-id or
-block-mask construction, so both the CPU oracle and the HIP path can be fed
-from it without sharing any of the method's code.
+segment ids given directly (long mixed-modality pack), episode token counts
+of unpadded packs, the random q, k, v, dO values and the random predictions /
+targets of the masked loss.  It holds none of the attention arithmetic and none
+of the seq-id, packing or block-mask construction, so both the CPU oracle and
+the HIP path can be fed from it without sharing any of the method's code.
 """
 from .packs import (  # noqa: F401
     PackSpec,
@@ -14,4 +15,7 @@ from .packs import (  # noqa: F401
     round_to_bf16,
     make_values,
     make_loss_values,
+    UNPADDED_BUDGET,
+    episode_stream,
+    unpadded_pack,
 )

@@ -28,6 +28,9 @@ __all__ = [
     "round_to_bf16",
     "make_values",
     "make_loss_values",
+    "UNPADDED_BUDGET",
+    "episode_stream",
+    "unpadded_pack",
 ]
 
 
@@ -52,12 +55,15 @@ class PackSpec:
     q_tokens_per_frame: int = 0
     kv_tokens_per_frame: int = 0
     segment_ids: Optional[np.ndarray] = None  # given directly (no frames)
+    token_lengths: Optional[np.ndarray] = None  # unpadded pack: tokens per episode
+    n_tokens: int = 0  # unpadded pack: fixed id-buffer length (the token budget)
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
     @property
     def cross(self) -> bool:
-        return self.segment_ids is None and self.q_tokens_per_frame != self.kv_tokens_per_frame
+        return (self.segment_ids is None and self.token_lengths is None
+                and self.q_tokens_per_frame != self.kv_tokens_per_frame)
 
     @property
     def n_episodes(self) -> int:
@@ -65,12 +71,16 @@ class PackSpec:
 
     @property
     def nq(self) -> int:
+        if self.token_lengths is not None:
+            return int(self.n_tokens)
         if self.segment_ids is not None:
             return int(len(self.segment_ids))
         return self.n_episodes * self.frames_padded * self.q_tokens_per_frame
 
     @property
     def nkv(self) -> int:
+        if self.token_lengths is not None:
+            return int(self.n_tokens)
         if self.segment_ids is not None:
             return int(len(self.segment_ids))
         return self.n_episodes * self.frames_padded * self.kv_tokens_per_frame
@@ -191,6 +201,25 @@ def bucketed_sweep(cross: bool = False, seed: int = 0, n_episodes: int = 160,
             q_tokens_per_frame=6 if cross else 32, kv_tokens_per_frame=32,
             notes="length-bucketed batch of 4"))
     return specs
+
+
+UNPADDED_BUDGET = 68_000  # tokens per GPU ("about 68k", LingBot-VA packing report, section 1)
+
+
+def episode_stream(seed: int = 0, n_episodes: int = 160, tokens_per_frame: int = 32):
+    """Token counts of a stream of episodes in arrival order: frames ~ U[103, 362]
+    (the same draw as ``bucketed_sweep``) times ``tokens_per_frame``, no padding."""
+    frames = np.random.default_rng(seed).integers(103, 363, n_episodes)
+    return (frames * int(tokens_per_frame)).astype(np.int32)
+
+
+def unpadded_pack(token_lengths, name: str = "unpadded-68k", budget: int = UNPADDED_BUDGET,
+                  heads: int = 24, head_dim: int = 128, seed=6) -> PackSpec:
+    """An unpadded pack of the given episodes (consumers build the ids from the
+    lengths) in an id buffer of ``budget`` tokens; values as the other bf16 packs."""
+    return PackSpec(name, heads=heads, head_dim=head_dim, dtype="bf16", seed=seed,
+                    value_std=0.5, token_lengths=np.asarray(token_lengths, np.int32),
+                    n_tokens=int(budget), notes="episodes back to back, no frame padding")
 
 
 CONFIG_NAMES = ("tiny-f32", "equal-4x120", "var-4x288", "bucketed", "long-64k")
