@@ -14,7 +14,9 @@ Readings taken (the page gives no formula):
   * on a packed sequence every episode (segment) has its own conditioning, so
     scale and shift are [S, D] tables and row i uses the row of its segment;
     segment s covers rows offsets[s] .. offsets[s+1]-1 (episodes are stored
-    back to back); rows past offsets[S] belong to no segment;
+    back to back); rows before offsets[0] or from offsets[S] on belong to no
+    segment; offsets are first clamped into [0, N] and made non-decreasing
+    (running maximum), so segments never overlap;
   * a row is valid iff its seq id is >= 0 and it lies in a segment; invalid
     rows (frame padding) give y = 0, mean = rstd = 0, dx = 0 and add nothing
     to the modulation gradients.
@@ -32,8 +34,12 @@ import numpy as np
 def segment_of_rows(offsets, n: int) -> np.ndarray:
     """Segment index of each of n rows (-1 outside every segment)."""
     seg = np.full(int(n), -1, dtype=np.int64)
-    for s in range(len(offsets) - 1):
-        for i in range(max(int(offsets[s]), 0), min(int(offsets[s + 1]), int(n))):
+    off = []
+    for o in list(offsets):
+        o = min(max(int(o), 0), int(n))
+        off.append(max(o, off[-1]) if off else o)
+    for s in range(len(off) - 1):
+        for i in range(off[s], off[s + 1]):
             seg[i] = s
     return seg
 

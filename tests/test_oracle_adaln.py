@@ -112,3 +112,9 @@ def test_padding_and_rows_outside_segments():
     dx2, dsh2, dsc2 = oada.backward(x2, dy2, ids, off, scale)
     assert np.array_equal(dsh, dsh2) and np.array_equal(dsc, dsc2)
     assert (dsh[1] == 0).all() and (dsc[1] == 0).all()      # empty segment 1
+
+
+def test_offsets_are_clamped_and_made_monotone():
+    seg = oada.segment_of_rows([-4, 3, 2, 7, 20], 10)      # -> 0, 3, 3, 7, 10
+    assert seg.tolist() == [0, 0, 0, 2, 2, 2, 2, 3, 3, 3]
+    assert oada.segment_of_rows([5, 5], 8).tolist() == [-1] * 8
