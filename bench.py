@@ -178,6 +178,56 @@ def bench_unpadded_pack(pa, iters=5):
             "tokens_per_s": round(int(sel.sum()) / (ms * 1e-3), 1)}
 
 
+def bench_adaln(pa, spec, ids, dim=3072, iters=20):
+    """Fused AdaLN forward and backward on the pack's rows (dim features, one
+    modulation row per episode), with the unfused torch chain timed beside it."""
+    import torch
+    n = spec.nq
+    dev = ids.device
+    g = torch.Generator(device=dev).manual_seed(5)
+    x = torch.randn((n, dim), generator=g, device=dev).to(torch.bfloat16)
+    dy = torch.randn((n, dim), generator=g, device=dev).to(torch.bfloat16)
+    S = spec.n_episodes
+    shift = 0.5 * torch.randn((S, dim), generator=g, device=dev)
+    scale = 0.5 * torch.randn((S, dim), generator=g, device=dev)
+    per = spec.frames_padded * spec.q_tokens_per_frame
+    off = (torch.arange(S + 1, device=dev, dtype=torch.int32) * per)
+    y, mean, rstd = pa.adaln_fwd(x, ids, off, shift, scale)
+    dx, dsh, dsc = pa.adaln_bwd(x, dy, ids, off, scale, mean, rstd)
+    ws = torch.empty(pa.adaln_bwd_workspace_bytes(n, dim, S), dtype=torch.uint8, device=dev)
+    fwd_ms = time_calls(lambda: pa.adaln_fwd(x, ids, off, shift, scale, out=(y, mean, rstd)),
+                        iters)
+    bwd_ms = time_calls(lambda: pa.adaln_bwd(x, dy, ids, off, scale, mean, rstd, ws,
+                                             out=(dx, dsh, dsc)), iters)
+    nv = int((ids >= 0).sum().item())
+    # algorithmic bytes: fwd reads valid x rows, writes every y row and the row
+    # statistics; bwd reads valid x, dy rows and their statistics, writes every
+    # dx row and the two modulation-gradient tables; ids read once per pass
+    fwd_bytes = 2 * dim * nv + 2 * dim * n + 8 * n + 4 * n + 8 * S * dim
+    bwd_bytes = 2 * 2 * dim * nv + 8 * nv + 2 * dim * n + 4 * n + 2 * 4 * S * dim + 4 * S * dim
+
+    seg = (torch.arange(n, device=dev) // per).clamp_max(S - 1)
+    valid = (ids >= 0).to(torch.bfloat16)[:, None]
+    xr = x.detach().clone().requires_grad_(True)
+    shr, scr = shift.clone().requires_grad_(True), scale.clone().requires_grad_(True)
+
+    def unfused():
+        xn = torch.nn.functional.layer_norm(xr, (dim,), eps=1e-6)
+        out = (xn * (1 + scr[seg]) + shr[seg]).to(torch.bfloat16) * valid
+        out.backward(dy)
+    unfused_ms = time_calls(unfused, max(iters // 4, 3))
+    fused_ms = fwd_ms + bwd_ms
+    return {"shape": f"{n} x {dim} bf16, {S} segments, {nv} valid rows",
+            "fwd_ms": round(fwd_ms, 4), "fwd_GBs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+            "fwd_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bwd_ms": round(bwd_ms, 4), "bwd_GBs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+            "bwd_frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes, "bound": "hbm",
+            "peak_GBs": PEAK_HBM_GBS,
+            "torch_unfused_fwd_bwd_ms": round(unfused_ms, 4),
+            "speedup_vs_unfused": round(unfused_ms / fused_ms, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +345,11 @@ def main():
         f"({100 * r['frac']:.1f}% of HBM peak)")
     extras["unpadded_pack"] = r = bench_unpadded_pack(pa)
     log(f"[bench] unpadded pack: {r['ms_per_step']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful")
+    extras["adaln"] = r = bench_adaln(pa, spec, ids)
+    log(f"[bench] adaln fwd {r['fwd_ms'] * 1e3:.1f} us {r['fwd_GBs']} GB/s, "
+        f"bwd {r['bwd_ms'] * 1e3:.1f} us {r['bwd_GBs']} GB/s; "
+        f"unfused torch fwd+bwd {r['torch_unfused_fwd_bwd_ms']:.3f} ms "
+        f"({r['speedup_vs_unfused']}x)")
 
     cpu = None
     if not args.no_cpu_baseline:

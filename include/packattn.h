@@ -272,6 +272,50 @@ int32_t masked_mse_fwd_bwd(int32_t dtype, int32_t n, int32_t C, const void* pred
                            float* stats, void* dpred, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * AdaLN on a packed sequence (AdaptiveLoad summary, section 2B: LayerNorm and
+ * modulation fused into one pass with the row statistics kept on chip; the
+ * backward reduces the modulation gradients over the sequence with feature
+ * tiles, each thread owning fixed feature columns down a tile of rows).
+ *
+ *   xhat = (x - mean) / sqrt(var + eps)        (per row over D, biased variance)
+ *   y    = xhat * (1 + scale[s]) + shift[s]    (s = segment of the row)
+ *   dx   = rstd * (g - mean_D(g) - xhat * mean_D(g * xhat)),  g = dy * (1 + scale[s])
+ *   d_scale[s] = sum over valid rows of s of dy * xhat,  d_shift[s] = sum of dy
+ *
+ * Segments: segment s (0 <= s < n_seg) is rows seg_offsets[s] .. seg_offsets[s+1]-1
+ * (episodes stored back to back, e.g. the offsets seq_ids_from_lengths
+ * returns, or b * frames_padded * tokens_per_frame for a frame-padded pack).
+ * The offsets are read clamped into [0, n] and made non-decreasing.  A row is
+ * valid iff it lies in a segment and seq_id >= 0; invalid rows give y = 0,
+ * dx = 0, mean = rstd = 0 and add nothing to d_shift / d_scale.  Results are
+ * bitwise reproducible (every sum has a fixed order).
+ *
+ *   dtype         PA_F32 or PA_BF16: x, y, dy, dx (modulation and statistics are fp32)
+ *   n, D          rows >= 0 and features, D a multiple of 8 in [8, 4096]
+ *   n_seg         segments, 0 .. 2048
+ *   eps           >= 0, added to the variance (1e-6 is the usual choice)
+ *   x, y, dy, dx  device [n][D] of dtype, 16-byte aligned
+ *   seq_id        device int32[n]
+ *   seg_offsets   device int32[n_seg + 1]
+ *   shift, scale  device fp32 [n_seg][D], 16-byte aligned
+ *   mean, rstd    device fp32 [n]: written by adaln_fwd, read by adaln_bwd
+ *   d_shift, d_scale  device fp32 [n_seg][D], written (all rows), 16-byte aligned
+ *   workspace     device buffer of >= adaln_bwd_workspace_bytes(n, D, n_seg)
+ *                 bytes, 256-byte aligned, overwritten (per-tile partial sums)
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIGN,
+ *         PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+int32_t adaln_fwd(int32_t dtype, int32_t n, int32_t D, int32_t n_seg, float eps, const void* x,
+                  const int32_t* seq_id, const int32_t* seg_offsets, const float* shift,
+                  const float* scale, void* y, float* mean, float* rstd, void* stream);
+size_t adaln_bwd_workspace_bytes(int32_t n, int32_t D, int32_t n_seg);
+int32_t adaln_bwd(int32_t dtype, int32_t n, int32_t D, int32_t n_seg, const void* x,
+                  const void* dy, const int32_t* seq_id, const int32_t* seg_offsets,
+                  const float* scale, const float* mean, const float* rstd, void* dx,
+                  float* d_shift, float* d_scale, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,9 @@ from .packattn import (  # noqa: F401
     PA_F32,
     BlockMask,
     PackAttnError,
+    adaln_bwd,
+    adaln_bwd_workspace_bytes,
+    adaln_fwd,
     attn_packed_bwd,
     attn_packed_bwd_dkdv,
     attn_packed_bwd_dq,

@@ -70,6 +70,10 @@ def _load() -> ctypes.CDLL:
                                        vp, vp, pm, vp, vp, vp]),
         "plan_token_packs": (i32, [vp, i32, ctypes.c_int64, vp, vp]),
         "seq_ids_from_lengths": (i32, [vp, i32, i32, vp, vp, vp]),
+        "adaln_fwd": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "adaln_bwd_workspace_bytes": (sz, [i32, i32, i32]),
+        "adaln_bwd": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                            vp]),
         "masked_mse_workspace_bytes": (sz, [i32]),
         "masked_mse_fwd": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
@@ -426,3 +430,72 @@ def masked_mse_fwd_bwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.T
                                    dpred.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                    _stream(pred)), "masked_mse_fwd_bwd")
     return stats, dpred
+
+
+# ----------------------------------------------------------------------- AdaLN
+def _adaln_args(x, seq_id, seg_offsets):
+    _need(x, "x")
+    if x.dtype not in _DTYPES or x.dim() != 2:
+        raise ValueError("x must be a [n, D] float32/bfloat16 tensor")
+    _need(seq_id, "seq_id", torch.int32, x.device)
+    _need(seg_offsets, "seg_offsets", torch.int32, x.device)
+    n, d = x.shape
+    if seq_id.numel() != n:
+        raise ValueError("seq_id must have one id per row")
+    return n, d, seg_offsets.numel() - 1
+
+
+def adaln_fwd(x: torch.Tensor, seq_id: torch.Tensor, seg_offsets: torch.Tensor,
+              shift: torch.Tensor, scale: torch.Tensor, eps: float = 1e-6,
+              out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Returns ``(y, mean, rstd)``: y like x, mean / rstd fp32 ``[n]``."""
+    n, d, n_seg = _adaln_args(x, seq_id, seg_offsets)
+    for name, t in (("shift", shift), ("scale", scale)):
+        _need(t, name, torch.float32, x.device)
+        if tuple(t.shape) != (n_seg, d):
+            raise ValueError(f"{name} must be [{n_seg}, {d}]")
+    if out is None:
+        y = torch.empty_like(x)
+        mean = torch.empty(n, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(n, dtype=torch.float32, device=x.device)
+    else:
+        y, mean, rstd = out
+    _check(_lib.adaln_fwd(_DTYPES[x.dtype], n, d, n_seg, float(eps), x.data_ptr(),
+                          seq_id.data_ptr(), seg_offsets.data_ptr(), shift.data_ptr(),
+                          scale.data_ptr(), y.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                          _stream(x)), "adaln_fwd")
+    return y, mean, rstd
+
+
+def adaln_bwd_workspace_bytes(n: int, d: int, n_seg: int) -> int:
+    return int(_lib.adaln_bwd_workspace_bytes(int(n), int(d), int(n_seg)))
+
+
+def adaln_bwd(x: torch.Tensor, dy: torch.Tensor, seq_id: torch.Tensor,
+              seg_offsets: torch.Tensor, scale: torch.Tensor, mean: torch.Tensor,
+              rstd: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+              out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Returns ``(dx, d_shift, d_scale)``."""
+    n, d, n_seg = _adaln_args(x, seq_id, seg_offsets)
+    _need(dy, "dy", x.dtype, x.device)
+    if dy.shape != x.shape:
+        raise ValueError("dy must match x")
+    _need(scale, "scale", torch.float32, x.device)
+    _need(mean, "mean", torch.float32, x.device)
+    _need(rstd, "rstd", torch.float32, x.device)
+    if out is None:
+        dx = torch.empty_like(x)
+        d_shift = torch.empty((n_seg, d), dtype=torch.float32, device=x.device)
+        d_scale = torch.empty((n_seg, d), dtype=torch.float32, device=x.device)
+    else:
+        dx, d_shift, d_scale = out
+    nbytes = adaln_bwd_workspace_bytes(n, d, n_seg)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, x.device)
+    _check(_lib.adaln_bwd(_DTYPES[x.dtype], n, d, n_seg, x.data_ptr(), dy.data_ptr(),
+                          seq_id.data_ptr(), seg_offsets.data_ptr(), scale.data_ptr(),
+                          mean.data_ptr(), rstd.data_ptr(), dx.data_ptr(), d_shift.data_ptr(),
+                          d_scale.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                          _stream(x)), "adaln_bwd")
+    return dx, d_shift, d_scale

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for want in ("seq_ids_from_valid_frames", "build_block_mask", "build_block_mask_bytes",
                  "attn_packed_fwd", "attn_packed_bwd", "attn_packed_bwd_workspace_bytes",
                  "pa_status_str", "masked_mse_fwd", "masked_mse_bwd", "masked_mse_fwd_bwd",
-                 "masked_mse_workspace_bytes"):
+                 "masked_mse_workspace_bytes", "adaln_fwd", "adaln_bwd", "plan_token_packs",
+                 "seq_ids_from_lengths"):
         assert want in names
 
 
@@ -195,3 +196,28 @@ def test_masked_loss_argument_errors(lib):
                                   None) == PA_ERR_NULL
     assert lib.masked_mse_fwd_bwd(1, 1000, 192, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, 16,
                                   None) == PA_ERR_WORKSPACE
+
+
+def test_adaln_argument_errors(lib):
+    assert lib.adaln_bwd_workspace_bytes(1000, 3072, 4) > 0
+    assert lib.adaln_bwd_workspace_bytes(1000, 3076, 4) == 0     # D not a multiple of 8
+    assert lib.adaln_bwd_workspace_bytes(1000, 4104, 4) == 0     # D > 4096
+    assert lib.adaln_bwd_workspace_bytes(1000, 64, 2049) == 0    # too many segments
+    f = lambda **kw: lib.adaln_fwd(kw.get("dt", 1), kw.get("n", 100), kw.get("d", 64),  # noqa: E731
+                                   kw.get("s", 2), kw.get("eps", 1e-6), kw.get("x", FAKE), FAKE,
+                                   kw.get("off", FAKE), FAKE, FAKE, kw.get("y", FAKE), FAKE,
+                                   FAKE, None)
+    assert f(dt=2) == PA_ERR_DTYPE
+    assert f(d=60) == PA_ERR_SHAPE
+    assert f(s=-1) == PA_ERR_SHAPE
+    assert f(eps=-1.0) == PA_ERR_SHAPE
+    assert f(eps=float("nan")) == PA_ERR_SHAPE
+    assert f(off=None) == PA_ERR_NULL
+    assert f(y=None) == PA_ERR_NULL
+    assert f(x=ctypes.c_void_p(0x100004)) == PA_ERR_ALIGN
+    ws = lib.adaln_bwd_workspace_bytes(100, 64, 2)
+    g = lambda **kw: lib.adaln_bwd(1, 100, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,  # noqa: E731
+                                   FAKE, FAKE, FAKE, kw.get("ws", FAKE), kw.get("nb", ws), None)
+    assert g(nb=ws - 1) == PA_ERR_WORKSPACE
+    assert g(ws=ctypes.c_void_p(0x100010)) == PA_ERR_ALIGN
+    assert g(ws=None) == PA_ERR_NULL

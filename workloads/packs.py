@@ -28,6 +28,7 @@ __all__ = [
     "round_to_bf16",
     "make_values",
     "make_loss_values",
+    "make_adaln_values",
     "UNPADDED_BUDGET",
     "episode_stream",
     "unpadded_pack",
@@ -136,6 +137,24 @@ def make_loss_values(n: int, channels: int, dtype: str, seed):
         a = rng.standard_normal((int(n), int(channels)), dtype=np.float32)
         out.append(round_to_bf16(a) if dtype == "bf16" else a)
     return tuple(out)
+
+
+def make_adaln_values(n: int, dim: int, n_seg: int, dtype: str, seed, mod_std: float = 0.5):
+    """Draw AdaLN inputs: x [n, dim] with a random scale in [0.5, 2) and offset
+    ~ N(0, 1) per row (so the normalisation has work to do), dy [n, dim] ~ N(0, 1),
+    and the per-segment modulation tables shift, scale [n_seg, dim] ~ N(0, mod_std)
+    (always fp32).  x and dy are rounded to bf16 for bf16.  Draw order: x, the
+    row scales, the row offsets, dy, shift, scale."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((int(n), int(dim)), dtype=np.float32)
+    x *= rng.uniform(0.5, 2.0, (int(n), 1)).astype(np.float32)
+    x += rng.standard_normal((int(n), 1), dtype=np.float32)
+    dy = rng.standard_normal((int(n), int(dim)), dtype=np.float32)
+    shift = (mod_std * rng.standard_normal((int(n_seg), int(dim)))).astype(np.float32)
+    scale = (mod_std * rng.standard_normal((int(n_seg), int(dim)))).astype(np.float32)
+    if dtype == "bf16":
+        x, dy = round_to_bf16(x), round_to_bf16(dy)
+    return x, dy, shift, scale
 
 
 def _pad_multiple(f: int, m: int = 8) -> int:
