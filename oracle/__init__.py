@@ -14,7 +14,8 @@ Pages cited (by title and section):
   * "Furniture packing, variable length" report -- implementation part: a
     seq id of -1 removes a token from attention as both query and key, and
     tokens only attend to tokens with the same seq id.
-  * AdaptiveLoad summary -- section 2B: the fused LayerNorm-Modulate (AdaLN)
+  * AdaptiveLoad summary -- section 2A: dual-constraint batch sizing and the
+    step-cost fit; section 2B: the fused LayerNorm-Modulate (AdaLN)
     operation and its modulation-gradient reduction over the sequence.
   * "LingBot-VA attention profiling" report -- next steps: the document-id
     mask predicate ``doc_id[q] == doc_id[k]``; conclusion: several episodes
@@ -25,6 +26,7 @@ Modules:
   packing    -- next-fit assignment of episodes to packs under a token budget
   loss       -- frame-valid masked squared-error loss and its gradient
   adaln      -- LayerNorm with per-segment modulation, forward and backward
+  sampler    -- length-bucket batch sampler, dual-constraint batch sizing, cost fit
   blockmask  -- per tile-pair valid-pair counts, classes and CSR lists
   attention  -- per-episode dense softmax attention and its gradients
 
@@ -32,4 +34,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against brute
 force, torch's fp64 attention with autograd, finite differences, closed forms
 and the pages' invariants; none is marked "parity unpinned".
 """
-from . import seqids, blockmask, attention, loss, packing, adaln  # noqa: F401
+from . import seqids, blockmask, attention, loss, packing, adaln, sampler  # noqa: F401
