@@ -228,6 +228,64 @@ def bench_adaln(pa, spec, ids, dim=3072, iters=20):
             "speedup_vs_unfused": round(unfused_ms / fused_ms, 2)}
 
 
+def bench_planner(pa, heads=24, head_dim=128, iters=3):
+    """Fit step time ~ a + b*B*S^p of the packed attention fwd+bwd (ids, mask,
+    forward, backward) to a scan of packs of B equal episodes of S tokens, then
+    plan the 160-episode stream with fixed batches of 4 and with the dual
+    constraint, and compare the spread of the predicted step times."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    budget = wl.UNPADDED_BUDGET
+    g = torch.Generator(device=dev).manual_seed(13)
+    big = (0.5 * torch.randn((4, budget, heads, head_dim), generator=g, device=dev)).to(
+        torch.bfloat16)
+    shapes = [(B, S) for S in (2048, 4096, 8192, 12288, 16384) for B in (1, 2, 4, 8)
+              if B * S <= budget]
+    Bs, Ss, ts = [], [], []
+    for B, S in shapes:
+        n = B * S
+        Q, K, V, DO = (big[j, :n] for j in range(4))
+        vf = torch.full((B,), S // 32, dtype=torch.int32, device=dev)
+
+        def step():
+            ids = pa.seq_ids_from_valid_frames(vf, S // 32, 32)
+            mask = pa.build_block_mask(ids, ids, 128, 128)
+            o, lse = pa.attn_packed_fwd(Q, K, V, ids, ids, mask)
+            pa.attn_packed_bwd(Q, K, V, o, DO, lse, ids, ids, mask)
+        Bs.append(B)
+        Ss.append(S)
+        ts.append(time_calls(step, iters, warmup=1))
+    a, b, p = pa.fit_step_cost(Bs, Ss, ts)
+    pred = [a + b * B * S ** p for B, S in zip(Bs, Ss)]
+    fit_err = max(abs(x - y) / y for x, y in zip(pred, ts))
+    # plan the episode stream: fixed batches of 4 vs the dual constraint with
+    # M_mem = the token budget and M_comp = 4 episodes of the median padded length
+    frames = (wl.episode_stream() // 32).tolist()
+    med = float(np.median([-(-f // 8) * 8 * 32 for f in frames]))
+    dual = (float(budget), 4.0 * med ** p, p, 32)
+
+    def cost_cov(batches, fpad):
+        c = np.array([a + b * len(bt) * (f * 32) ** p for bt, f in zip(batches, fpad)])
+        per_ep = c.sum() / sum(len(bt) for bt in batches)
+        return float(c.std() / c.mean()), len(batches), float(per_ep)
+    fixed = pa.length_bucket_batches(frames, 0, 0, 200, 8, 4)
+    dualb = pa.length_bucket_batches(frames, 0, 0, 200, 8, 0, dual=dual)
+    cf, nf, ef = cost_cov(*fixed)
+    cd, nd, ed = cost_cov(*dualb)
+    return {"scan": [{"B": B, "S": S, "ms": round(t, 4)} for B, S, t in zip(Bs, Ss, ts)],
+            "fit": {"a_ms": round(a, 5), "b_ms": b, "p": round(p, 4),
+                    "max_rel_err": round(fit_err, 4)},
+            "plan_160_episodes": {
+                "fixed_batch_4": {"batches": nf, "cost_cov": round(cf, 4),
+                                  "pred_ms_per_episode": round(ef, 4)},
+                "dual_constraint": {"batches": nd, "cost_cov": round(cd, 4),
+                                    "pred_ms_per_episode": round(ed, 4),
+                                    "m_mem_tokens": budget, "m_comp": dual[1]}}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +403,11 @@ def main():
         f"({100 * r['frac']:.1f}% of HBM peak)")
     extras["unpadded_pack"] = r = bench_unpadded_pack(pa)
     log(f"[bench] unpadded pack: {r['ms_per_step']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful")
+    extras["planner"] = r = bench_planner(pa)
+    log(f"[bench] planner fit a={r['fit']['a_ms']} ms p={r['fit']['p']} "
+        f"(max rel err {r['fit']['max_rel_err']}); cost CoV fixed "
+        f"{r['plan_160_episodes']['fixed_batch_4']['cost_cov']} -> dual "
+        f"{r['plan_160_episodes']['dual_constraint']['cost_cov']}")
     extras["adaln"] = r = bench_adaln(pa, spec, ids)
     log(f"[bench] adaln fwd {r['fwd_ms'] * 1e3:.1f} us {r['fwd_GBs']} GB/s, "
         f"bwd {r['bwd_ms'] * 1e3:.1f} us {r['bwd_GBs']} GB/s; "

@@ -316,6 +316,63 @@ int32_t adaln_bwd(int32_t dtype, int32_t n, int32_t D, int32_t n_seg, const void
                   float* d_shift, float* d_scale, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/*
+ * Batch planning -- HOST functions (host pointers; no device work).
+ *
+ * length_bucket_batches: one rank's batches for one epoch ("LingBot-VA packing"
+ * report, section 2.1, LengthBucketBatchSampler and the pad collate):
+ *   1. the episodes 0 .. n-1 are shuffled (Fisher-Yates driven by SplitMix64
+ *      seeded with seed + epoch; j = high 64 bits of next() * (i + 1));
+ *   2. the list is padded to a multiple of world_size by repeating it from
+ *      its start; rank r takes positions r, r + world_size, ... (every rank
+ *      gets the same count, length_bucket_rank_size(n, world_size));
+ *   3. the rank's list is cut into pools of pool_size episodes, each pool is
+ *      sorted by frames (ascending, stable) and cut into batches: batch_size
+ *      episodes (the pool's last batch may be short), or, with batch_size = 0,
+ *      greedily under the dual constraint below (a batch grows while its size
+ *      is within dual_constraint_batch of its padded sequence length
+ *      round_up(max frames, pad_multiple) * tokens_per_frame);
+ *   4. the batch order is shuffled, continuing the same generator.
+ *   frames        host int32[n], latent frames per episode (>= 0)
+ *   episodes      host int32[length_bucket_rank_size(n, W)], written: the
+ *                 episodes of all batches, batch after batch
+ *   batch_ptr     host int32[that + 1], written: batch b is
+ *                 episodes[batch_ptr[b] .. batch_ptr[b+1])
+ *   batch_frames  host int32[that], written: padded frames of each batch,
+ *                 round_up(max frames, pad_multiple)
+ *   n_batches     host int32, written
+ *   Errors: PA_ERR_SHAPE (n < 0, pool_size < 1, pad_multiple < 1, batch_size < 0,
+ *           rank outside [0, world_size), a negative frame count, bad dual
+ *           parameters), PA_ERR_NULL (NULL outputs, or dual NULL with batch_size 0).
+ *
+ * dual_constraint_batch: AdaptiveLoad summary, section 2A: the batch size of a
+ *   bucket of sequence length S, max(1, min(floor(m_mem / S), floor(m_comp / S^p))),
+ *   from B * S <= m_mem (memory, linear) and B * S^p <= m_comp (compute).
+ *   Returns the batch size (>= 1) or PA_ERR_SHAPE for non-positive S, m_mem, m_comp.
+ *
+ * fit_step_cost: fits step time t ~ a + b * B * S^p to m >= 2 measured shapes
+ *   (same section: the step-cost model behind p and m_comp) by least squares in
+ *   t: for each p the best a, b are a straight-line fit, and p in [p_lo, p_hi]
+ *   minimises the residual (golden-section search).  out = {a, b, p}.
+ *   Errors: PA_ERR_SHAPE (m < 2, empty range, a non-positive B or S), PA_ERR_NULL.
+ */
+typedef struct pa_dual_constraint {
+  double m_mem;             /* token budget per batch (memory constraint)        */
+  double m_comp;            /* compute budget: B * S^p <= m_comp                  */
+  double p;                 /* cost exponent                                      */
+  int32_t tokens_per_frame; /* sequence length S = padded frames * this          */
+} pa_dual_constraint;
+
+size_t length_bucket_rank_size(int32_t n, int32_t world_size);
+int32_t length_bucket_batches(const int32_t* frames, int32_t n, uint64_t seed, int32_t epoch,
+                              int32_t pool_size, int32_t pad_multiple, int32_t batch_size,
+                              const pa_dual_constraint* dual, int32_t rank, int32_t world_size,
+                              int32_t* episodes, int32_t* batch_ptr, int32_t* batch_frames,
+                              int32_t* n_batches);
+int32_t dual_constraint_batch(double seq_len, double m_mem, double m_comp, double p);
+int32_t fit_step_cost(const double* B, const double* S, const double* t, int32_t m, double p_lo,
+                      double p_hi, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,9 @@ from .packattn import (  # noqa: F401
     attn_packed_fwd,
     build_block_mask,
     build_block_mask_bytes,
+    dual_constraint_batch,
+    fit_step_cost,
+    length_bucket_batches,
     masked_mse_bwd,
     masked_mse_fwd,
     masked_mse_fwd_bwd,

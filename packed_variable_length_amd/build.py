@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpackattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["seq_ids.hip", "block_mask.hip", "attn_fwd.hip", "attn_bwd.hip", "masked_loss.hip", "packing.hip",
-           "adaln.hip"]
+           "adaln.hip", "planner.cpp"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -31,6 +31,13 @@ class PackAttnError(RuntimeError):
         super().__init__(f"{where}: {pa_status_str(status)} ({status})")
 
 
+class PaDualConstraint(ctypes.Structure):
+    """Mirror of ``pa_dual_constraint``."""
+
+    _fields_ = [("m_mem", ctypes.c_double), ("m_comp", ctypes.c_double), ("p", ctypes.c_double),
+                ("tokens_per_frame", ctypes.c_int32)]
+
+
 class PaBlockMask(ctypes.Structure):
     """Mirror of ``pa_block_mask`` (host descriptor of device storage)."""
 
@@ -74,6 +81,12 @@ def _load() -> ctypes.CDLL:
         "adaln_bwd_workspace_bytes": (sz, [i32, i32, i32]),
         "adaln_bwd": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                             vp]),
+        "length_bucket_rank_size": (sz, [i32, i32]),
+        "length_bucket_batches": (i32, [vp, i32, ctypes.c_uint64, i32, i32, i32, i32, vp, i32,
+                                        i32, vp, vp, vp, vp]),
+        "dual_constraint_batch": (i32, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_double]),
+        "fit_step_cost": (i32, [vp, vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]),
         "masked_mse_workspace_bytes": (sz, [i32]),
         "masked_mse_fwd": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
@@ -499,3 +512,48 @@ def adaln_bwd(x: torch.Tensor, dy: torch.Tensor, seq_id: torch.Tensor,
                           d_scale.data_ptr(), workspace.data_ptr(), workspace.numel(),
                           _stream(x)), "adaln_bwd")
     return dx, d_shift, d_scale
+
+
+# -------------------------------------------------------------- batch planning
+def length_bucket_batches(frames, seed: int, epoch: int, pool_size: int, pad_multiple: int = 8,
+                          batch_size: int = 4, dual=None, rank: int = 0, world_size: int = 1):
+    """One rank's batches for one epoch (host).  ``dual = (m_mem, m_comp, p,
+    tokens_per_frame)`` with ``batch_size = 0`` sizes batches by the dual
+    constraint.  Returns (list of episode-index lists, padded frames per batch)."""
+    import numpy as np
+    fr = np.ascontiguousarray(np.asarray(frames, dtype=np.int32))
+    n = len(fr)
+    cap = int(_lib.length_bucket_rank_size(n, int(world_size)))
+    eps = np.empty(max(cap, 1), np.int32)
+    ptr = np.empty(cap + 1, np.int32)
+    bfr = np.empty(max(cap, 1), np.int32)
+    nb = ctypes.c_int32(0)
+    d = None
+    if dual is not None:
+        d = PaDualConstraint(float(dual[0]), float(dual[1]), float(dual[2]), int(dual[3]))
+    _check(_lib.length_bucket_batches(fr.ctypes.data if n else None, n, int(seed) & (2**64 - 1),
+                                      int(epoch), int(pool_size), int(pad_multiple),
+                                      int(batch_size), ctypes.byref(d) if d is not None else None,
+                                      int(rank), int(world_size), eps.ctypes.data,
+                                      ptr.ctypes.data, bfr.ctypes.data, ctypes.byref(nb)),
+           "length_bucket_batches")
+    k = nb.value
+    batches = [eps[ptr[b]:ptr[b + 1]].tolist() for b in range(k)]
+    return batches, bfr[:k].tolist()
+
+
+def dual_constraint_batch(seq_len: float, m_mem: float, m_comp: float, p: float) -> int:
+    r = int(_lib.dual_constraint_batch(float(seq_len), float(m_mem), float(m_comp), float(p)))
+    _check(min(r, 0), "dual_constraint_batch")
+    return r
+
+
+def fit_step_cost(B, S, t, p_lo: float = 1.0, p_hi: float = 3.0):
+    """Least-squares fit of t ~ a + b * B * S^p (host); returns (a, b, p)."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(np.asarray(v, dtype=np.float64)) for v in (B, S, t)]
+    out = np.empty(3, np.float64)
+    _check(_lib.fit_step_cost(arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data,
+                              len(arrs[2]), float(p_lo), float(p_hi), out.ctypes.data),
+           "fit_step_cost")
+    return float(out[0]), float(out[1]), float(out[2])

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                  "attn_packed_fwd", "attn_packed_bwd", "attn_packed_bwd_workspace_bytes",
                  "pa_status_str", "masked_mse_fwd", "masked_mse_bwd", "masked_mse_fwd_bwd",
                  "masked_mse_workspace_bytes", "adaln_fwd", "adaln_bwd", "plan_token_packs",
-                 "seq_ids_from_lengths"):
+                 "seq_ids_from_lengths", "length_bucket_batches", "dual_constraint_batch",
+                 "fit_step_cost"):
         assert want in names
 
 
