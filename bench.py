@@ -286,6 +286,25 @@ def bench_planner(pa, heads=24, head_dim=128, iters=3):
                                     "m_mem_tokens": budget, "m_comp": dual[1]}}}
 
 
+def run_extras(pa, spec, ids, extras):
+    """The measurements of the loss, unpadded-pack, planner and AdaLN rows."""
+    extras["masked_loss"] = r = bench_masked_loss(pa, ids)
+    log(f"[bench] masked_loss: {r['avg_call_ms'] * 1e3:.1f} us, {r['achieved_GBs']} GB/s "
+        f"({100 * r['frac']:.1f}% of HBM peak)")
+    extras["unpadded_pack"] = r = bench_unpadded_pack(pa)
+    log(f"[bench] unpadded pack: {r['ms_per_step']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful")
+    extras["planner"] = r = bench_planner(pa)
+    log(f"[bench] planner fit a={r['fit']['a_ms']} ms p={r['fit']['p']} "
+        f"(max rel err {r['fit']['max_rel_err']}); cost CoV fixed "
+        f"{r['plan_160_episodes']['fixed_batch_4']['cost_cov']} -> dual "
+        f"{r['plan_160_episodes']['dual_constraint']['cost_cov']}")
+    extras["adaln"] = r = bench_adaln(pa, spec, ids)
+    log(f"[bench] adaln fwd {r['fwd_ms'] * 1e3:.1f} us {r['fwd_GBs']} GB/s, "
+        f"bwd {r['bwd_ms'] * 1e3:.1f} us {r['bwd_GBs']} GB/s; "
+        f"unfused torch fwd+bwd {r['torch_unfused_fwd_bwd_ms']:.3f} ms "
+        f"({r['speedup_vs_unfused']}x)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +314,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=str, default="0,1,2,3,4,5,6,7",
                     help="heads the oracle baseline computes (a bounded sample)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the loss / unpadded-pack / planner / AdaLN measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -397,22 +418,9 @@ def main():
                 "avg_launch_ms": round(kernels[dom], 4),
                 "source_sha256": source_sha256(dom)}
 
-    extras = {"masked_loss": bench_masked_loss(pa, ids)}
-    r = extras["masked_loss"]
-    log(f"[bench] masked_loss: {r['avg_call_ms'] * 1e3:.1f} us, {r['achieved_GBs']} GB/s "
-        f"({100 * r['frac']:.1f}% of HBM peak)")
-    extras["unpadded_pack"] = r = bench_unpadded_pack(pa)
-    log(f"[bench] unpadded pack: {r['ms_per_step']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful")
-    extras["planner"] = r = bench_planner(pa)
-    log(f"[bench] planner fit a={r['fit']['a_ms']} ms p={r['fit']['p']} "
-        f"(max rel err {r['fit']['max_rel_err']}); cost CoV fixed "
-        f"{r['plan_160_episodes']['fixed_batch_4']['cost_cov']} -> dual "
-        f"{r['plan_160_episodes']['dual_constraint']['cost_cov']}")
-    extras["adaln"] = r = bench_adaln(pa, spec, ids)
-    log(f"[bench] adaln fwd {r['fwd_ms'] * 1e3:.1f} us {r['fwd_GBs']} GB/s, "
-        f"bwd {r['bwd_ms'] * 1e3:.1f} us {r['bwd_GBs']} GB/s; "
-        f"unfused torch fwd+bwd {r['torch_unfused_fwd_bwd_ms']:.3f} ms "
-        f"({r['speedup_vs_unfused']}x)")
+    extras = {}
+    if not args.no_extras:
+        run_extras(pa, spec, ids, extras)
 
     cpu = None
     if not args.no_cpu_baseline:
