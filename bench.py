@@ -32,6 +32,9 @@ KERNEL_SOURCES = {  # the files a kernel's code comes from (hashed to validate t
     "fwd": ["packed_variable_length_amd/csrc/attn_fwd.hip"],
     "bwd_dq": ["packed_variable_length_amd/csrc/attn_bwd.hip"],
     "bwd_dkdv": ["packed_variable_length_amd/csrc/attn_bwd.hip"],
+    "adaln_fwd": ["packed_variable_length_amd/csrc/adaln.hip"],
+    "adaln_bwd": ["packed_variable_length_amd/csrc/adaln.hip"],
+    "masked_loss": ["packed_variable_length_amd/csrc/masked_loss.hip"],
 }
 COMMON_SOURCES = ["packed_variable_length_amd/csrc/pa_tile.h",
                   "packed_variable_length_amd/csrc/pa_common.h"]
@@ -129,6 +132,7 @@ def bench_masked_loss(pa, ids, channels=192, iters=50):
     # every gradient row (zeros on padding rows); partials are negligible
     nbytes = 2 * 4 * n + 2 * 2 * channels * nv + 2 * channels * n
     return {"entry": "masked_mse_fwd_bwd", "shape": f"{n} x {channels} bf16, {nv} valid rows",
+            "traffic": measured_traffic("masked_loss", f"latent-{n}x{channels}"),
             "avg_call_ms": round(ms, 5), "algorithmic_bytes": nbytes,
             "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
             "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
@@ -223,6 +227,8 @@ def bench_adaln(pa, spec, ids, dim=3072, iters=20):
             "bwd_ms": round(bwd_ms, 4), "bwd_GBs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
             "bwd_frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes, "bound": "hbm",
+            "fwd_traffic": measured_traffic("adaln_fwd", f"adaln-{n}x{dim}"),
+            "bwd_traffic": measured_traffic("adaln_bwd", f"adaln-{n}x{dim}"),
             "peak_GBs": PEAK_HBM_GBS,
             "torch_unfused_fwd_bwd_ms": round(unfused_ms, 4),
             "speedup_vs_unfused": round(unfused_ms / fused_ms, 2)}
