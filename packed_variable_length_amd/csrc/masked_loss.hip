@@ -80,7 +80,7 @@ __device__ __forceinline__ Range block_rows(int n, int rows_per) {
 
 // Valid-row count of this block's row range, into cnt_part[blockIdx.x].
 __global__ void __launch_bounds__(kLossThreads)
-count_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t rows_per,
+loss_count_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t rows_per,
              uint32_t* __restrict__ cnt_part) {
   __shared__ uint32_t red[kLossThreads / 64];
   const Range rg = block_rows(n, rows_per);
@@ -95,7 +95,7 @@ count_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t rows_per,
 // gradient rows (scale from the finished counts in cnt_part).
 template <typename T, bool COUNT, bool GRAD>
 __global__ void __launch_bounds__(kLossThreads)
-sse_kernel(const T* __restrict__ pred, const T* __restrict__ target,
+loss_sse_kernel(const T* __restrict__ pred, const T* __restrict__ target,
            const int32_t* __restrict__ ids, int32_t n, int32_t c, int32_t rows_per, int32_t nparts,
            float upstream, float* __restrict__ sse_part, uint32_t* __restrict__ cnt_part,
            T* __restrict__ dpred) {
@@ -108,7 +108,7 @@ sse_kernel(const T* __restrict__ pred, const T* __restrict__ target,
     uint32_t total = 0;
     for (int i = threadIdx.x; i < nparts; i += kLossThreads) total += cnt_part[i];
     total = block_sum(total, redu);
-    // same rounding as finish_kernel's stats[3] times upstream (masked_mse_bwd)
+    // same rounding as loss_finish_kernel's stats[3] times upstream (masked_mse_bwd)
     k = total > 0 ? (float)(2.0 / ((double)total * (double)c)) * upstream : 0.f;
   }
   float sse = 0.f;
@@ -147,7 +147,7 @@ sse_kernel(const T* __restrict__ pred, const T* __restrict__ target,
 
 // One workgroup: stats = {loss, sum of squared errors, n_valid, grad factor}.
 __global__ void __launch_bounds__(kLossThreads)
-finish_kernel(const float* __restrict__ sse_part, const uint32_t* __restrict__ cnt_part,
+loss_finish_kernel(const float* __restrict__ sse_part, const uint32_t* __restrict__ cnt_part,
               int32_t nparts, int32_t c, float* __restrict__ stats) {
   __shared__ float redf[kLossThreads / 64];
   __shared__ uint32_t redu[kLossThreads / 64];
@@ -171,7 +171,7 @@ finish_kernel(const float* __restrict__ sse_part, const uint32_t* __restrict__ c
 // Gradient only, from the factor stats[3] of a finished forward.
 template <typename T>
 __global__ void __launch_bounds__(kLossThreads)
-grad_kernel(const T* __restrict__ pred, const T* __restrict__ target,
+loss_grad_kernel(const T* __restrict__ pred, const T* __restrict__ target,
             const int32_t* __restrict__ ids, int32_t n, int32_t c, int32_t rows_per,
             const float* __restrict__ stats, float upstream, T* __restrict__ dpred) {
   const Range rg = block_rows(n, rows_per);
@@ -219,10 +219,10 @@ template <typename T>
 void launch_fwd(const void* pred, const void* target, const int32_t* ids, int32_t n, int32_t c,
                 float* sse_part, uint32_t* cnt_part, float* stats, hipStream_t s) {
   if (n > 0)
-    hipLaunchKernelGGL((sse_kernel<T, true, false>), dim3(kLossBlocks), dim3(kLossThreads), 0, s,
+    hipLaunchKernelGGL((loss_sse_kernel<T, true, false>), dim3(kLossBlocks), dim3(kLossThreads), 0, s,
                        (const T*)pred, (const T*)target, ids, n, c, rows_per_block(n),
                        kLossBlocks, 0.f, sse_part, cnt_part, (T*)nullptr);
-  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLossThreads), 0, s, sse_part, cnt_part,
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(kLossThreads), 0, s, sse_part, cnt_part,
                      n > 0 ? kLossBlocks : 0, c, stats);
 }
 
@@ -232,13 +232,13 @@ void launch_fused(const void* pred, const void* target, const int32_t* ids, int3
                   hipStream_t s) {
   const int rp = rows_per_block(n);
   if (n > 0) {
-    hipLaunchKernelGGL(count_kernel, dim3(kLossBlocks), dim3(kLossThreads), 0, s, ids, n, rp,
+    hipLaunchKernelGGL(loss_count_kernel, dim3(kLossBlocks), dim3(kLossThreads), 0, s, ids, n, rp,
                        cnt_part);
-    hipLaunchKernelGGL((sse_kernel<T, false, true>), dim3(kLossBlocks), dim3(kLossThreads), 0, s,
+    hipLaunchKernelGGL((loss_sse_kernel<T, false, true>), dim3(kLossBlocks), dim3(kLossThreads), 0, s,
                        (const T*)pred, (const T*)target, ids, n, c, rp, kLossBlocks, upstream,
                        sse_part, cnt_part, (T*)dpred);
   }
-  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLossThreads), 0, s, sse_part, cnt_part,
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(kLossThreads), 0, s, sse_part, cnt_part,
                      n > 0 ? kLossBlocks : 0, c, stats);
 }
 
@@ -275,11 +275,11 @@ extern "C" int32_t masked_mse_bwd(int32_t dtype, int32_t n, int32_t c, const voi
   hipStream_t s = (hipStream_t)stream;
   const int rp = rows_per_block(n);
   if (dtype == PA_BF16)
-    hipLaunchKernelGGL(grad_kernel<uint16_t>, dim3(kLossBlocks), dim3(kLossThreads), 0, s,
+    hipLaunchKernelGGL(loss_grad_kernel<uint16_t>, dim3(kLossBlocks), dim3(kLossThreads), 0, s,
                        (const uint16_t*)pred, (const uint16_t*)target, seq_id, n, c, rp, stats,
                        upstream, (uint16_t*)dpred);
   else
-    hipLaunchKernelGGL(grad_kernel<float>, dim3(kLossBlocks), dim3(kLossThreads), 0, s,
+    hipLaunchKernelGGL(loss_grad_kernel<float>, dim3(kLossBlocks), dim3(kLossThreads), 0, s,
                        (const float*)pred, (const float*)target, seq_id, n, c, rp, stats,
                        upstream, (float*)dpred);
   return launch_status();
