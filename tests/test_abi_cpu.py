@@ -222,3 +222,15 @@ def test_adaln_argument_errors(lib):
     assert g(nb=ws - 1) == PA_ERR_WORKSPACE
     assert g(ws=ctypes.c_void_p(0x100010)) == PA_ERR_ALIGN
     assert g(ws=None) == PA_ERR_NULL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits non-zero with a message,
+    before anything touches a device."""
+    import subprocess
+    import sys
+    bench = os.path.join(ROOT, "bench.py")
+    r = subprocess.run([sys.executable, bench, "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr and r.stdout == ""
