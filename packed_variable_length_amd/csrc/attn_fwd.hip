@@ -7,9 +7,10 @@
 // of its query tile (block sparsity from the seq ids, "LingBot-VA packing"
 // report, section 2.2) and applies the elementwise mask only on partial tiles.
 //
-// bf16 kernels (gfx950 MFMA).  128-wide heads use the ping-pong kernel below
-// (8 waves per query tile, MFMA and softmax phases alternating between two
-// wave groups); 64-wide heads use the 4-wave kernel described here.
+// bf16 kernels (gfx950 MFMA).  128-wide heads use the paired ping-pong kernel
+// below (8 waves per pair of query tiles, MFMA and softmax phases alternating
+// between two wave groups); 64-wide heads use the 4-wave kernel described here.
+// Both compute in the same layout.
 //
 // 4-wave kernel: a workgroup of 4 waves owns one 128-row query tile
 // of one head; wave w owns query rows 32w..32w+31.  The scores are computed
@@ -25,6 +26,7 @@
 //
 // fp32 kernel: a plain one-thread-per-query-row loop with K/V staged in LDS,
 // exact expf; it serves fp32 inputs (correctness path).
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -212,80 +214,109 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// Ping-pong variant: a workgroup of 8 waves per 128-row query tile.  Wave w
-// owns query rows 32(w%4)..+31 and one half of every 128-key tile: waves 0-3
-// (group A) keys 0-63, waves 4-7 (group B) keys 64-127, each with its own
-// online-softmax state; the two halves are merged at the end.  Work alternates
-// in phases separated by barriers: while one group runs its MFMAs (the previous
-// tile's PV and this tile's scores) the other runs its softmax on the VALU, and
-// the next phase swaps.  Waves w and w+4 sit on the same SIMD (waves are dealt
-// to the SIMDs in order), so every SIMD has one MFMA wave and one VALU wave at
-// a time instead of two waves that drift into the same phase.
-//
-// Each group stages only its own half of the K and V tiles (K one tile ahead,
-// V one tile behind, two buffers each), one direct load at a time between the
-// instructions of its first phase of the step -- group A between its MFMAs,
-// group B between its softmax instructions -- so the loads of all eight waves
-// never queue up at once in front of the CU's address unit.
-constexpr int kPPTile = 128 * kRowBytes;  // one 128-key tile (32 KB)
-constexpr int kPPIds = 512;               // 128 key ids after a K tile
-constexpr int kPPHalf = 64 * kRowBytes;   // one group's 64 keys of a tile
+// Direct global->LDS loads issued from inline assembly.  The compiler does
+// not see these LDS writes, so it cannot answer them with conservative
+// vmcnt(0) waits in front of unrelated LDS reads (it did with the builtins
+// once three buffers of each kind were in flight); every use is ordered by
+// explicit vmcnt waits and barriers instead.  A kernel that uses them issues
+// no other LDS-DMA (they set M0 themselves).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Buffer resource over the rows row0 .. n - 1 of a [n][rs] bf16 tensor: reads
-// at or past row n return zeros (the hardware's range check), so a tail tile
-// needs no clamping.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* g, size_t rs, int row0,
-                                                            int n) {
-  const uint64_t bytes = row0 < n ? (uint64_t)(n - row0) * rs * 2 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(g + (size_t)row0 * rs), 0,
-                                           (int)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes),
-                                           0x00020000);
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One direct load of row group `blk` (rows 4 blk .. 4 blk + 3, 1 KB) of a
-// 64-row half tile: lane i fetches the 16 bytes that land at offset 16 i of
-// the group (the swizzled chunk of its row); `lane_off` is the lane's byte
-// offset inside row group 0, which does not depend on blk.  No per-lane address
-// arithmetic beyond one add, so it can sit between the MFMAs or VALU
-// instructions of a phase.
-__device__ __forceinline__ void stage_piece(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off,
-                                            uint32_t group_bytes, char* half_tile, int blk) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(half_tile + blk * 1024), 16,
-                                           lane_off + blk * group_bytes, 0, 0, 0);
+// raw buffer descriptor over `bytes` bytes from `base` (range-checked loads)
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
+
+// 16 bytes per lane from rsrc at byte offset voff to LDS (lane i at lds + 16 i)
+__device__ __forceinline__ void dma_b128(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
+// 4 bytes per lane from the lane's address to LDS (lane i at lds + 4 i)
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               ::"v"(src), "s"(lds) : "memory");
+}
+
+// Paired ping-pong variant: a workgroup of 8 waves per PAIR of query tiles,
+// the tiles at positions 2w and 2w + 1 of the longest-first order (equal or
+// nearly equal key lists: for contiguous segments, two tiles of one segment).
+// Group A (waves 0-3) owns the first tile, group B (waves 4-7) the second,
+// wave w query rows 32(w%4)..+31 of its group's tile, each over all keys.  Both
+// groups walk the same 64-key sub-tiles, one phase apart (A: MFMA phase then
+// softmax; B: softmax then MFMA phase), so each K/V sub-tile staged in LDS
+// serves 256 query rows: half the staging traffic per flop of one tile per
+// workgroup.  The sub-tiles cover each tile's key-tile range [first, last] of
+// its list -- one range when the two overlap or touch, else both ranges one
+// after the other; a tile in the walk that is not in a group's list is fully
+// masked for that group (class 0).
+constexpr int kPrSub = 64 * kRowBytes;  // one 64-key sub-tile (16 KB)
 
 template <int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, const int32_t* __restrict__ q_ids,
-                   const int32_t* __restrict__ kv_ids, int32_t nq, int32_t nkv, int32_t H,
-                   float s2, const uint8_t* __restrict__ tile_class,
-                   const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ q_cols,
-                   const int32_t* __restrict__ q_order, int32_t nkt, uint16_t* __restrict__ o,
-                   float* __restrict__ lse) {
-  static_assert(D == 128, "the ping-pong forward is laid out for 128-wide heads");
+fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, const int32_t* __restrict__ q_ids,
+                     const int32_t* __restrict__ kv_ids, int32_t nq, int32_t nkv, int32_t H,
+                     float s2, const uint8_t* __restrict__ tile_class,
+                     const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ q_cols,
+                     const int32_t* __restrict__ q_order, int32_t nkt,
+                     uint16_t* __restrict__ o, float* __restrict__ lse) {
+  static_assert(D == 128, "the paired forward is laid out for 128-wide heads");
   constexpr int kDB = D / 32, kKK = D / 16;
-  // separate arrays, so the compiler sees that the reads of one buffer never
-  // wait for the direct loads into another
-  __shared__ __attribute__((aligned(1024))) char kb0[kPPTile + kPPIds];
-  __shared__ __attribute__((aligned(1024))) char kb1[kPPTile + kPPIds];
-  __shared__ __attribute__((aligned(1024))) char vb0[kPPTile];
-  __shared__ __attribute__((aligned(1024))) char vb1[kPPTile];
+  __shared__ __attribute__((aligned(1024))) char kb0[kPrSub + 256];
+  __shared__ __attribute__((aligned(1024))) char kb1[kPrSub + 256];
+  __shared__ __attribute__((aligned(1024))) char kb2[kPrSub + 256];
+  __shared__ __attribute__((aligned(1024))) char vb0[kPrSub];
+  __shared__ __attribute__((aligned(1024))) char vb1[kPrSub];
+  __shared__ __attribute__((aligned(1024))) char vb2[kPrSub];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
   const int grp = wv >> 2, wq = wv & 3;
+  const int nqt = (nq + 127) / 128;
   int work, h;
-  block_work(blockIdx.x, H, (nq + 127) / 128, &work, &h);
-  const int qt = q_order[work];
-  const int beg = q_ptr[qt];
-  const int n = q_ptr[qt + 1] - beg;  // key tiles of this query tile
+  block_work(blockIdx.x, H, (nqt + 1) / 2, &work, &h);
+  const int qpair[2] = {q_order[2 * work], 2 * work + 1 < nqt ? q_order[2 * work + 1] : -1};
+  const int qmine = qpair[grp];  // -1: no tile (odd tile count), no rows, all masked
+  // key-tile ranges of the two lists (empty: first > last)
+  int first[2], last[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    first[g] = INT_MAX;
+    last[g] = -1;
+    if (qpair[g] >= 0 && q_ptr[qpair[g] + 1] > q_ptr[qpair[g]]) {
+      first[g] = q_cols[q_ptr[qpair[g]]];
+      last[g] = q_cols[q_ptr[qpair[g] + 1] - 1];
+    }
+  }
+  // the walk: segment 0 = [lo0, lo0 + len0), then segment 1 = [lo1, lo1 + len1)
+  int lo0, len0, lo1 = 0, len1 = 0;
+  if (last[1] < 0 || (last[0] >= 0 && first[1] <= last[0] + 1 && first[0] <= last[1] + 1)) {
+    lo0 = min(first[0], first[1]);  // one range (or only one list)
+    len0 = max(last[0], last[1]) - lo0 + 1;
+  } else if (last[0] < 0) {
+    lo0 = first[1];
+    len0 = last[1] - first[1] + 1;
+  } else {
+    const int g0 = first[0] <= first[1] ? 0 : 1;
+    lo0 = first[g0];
+    len0 = last[g0] - first[g0] + 1;
+    lo1 = first[1 - g0];
+    len1 = last[1 - g0] - first[1 - g0] + 1;
+  }
+  if (len0 < 0) len0 = 0;  // both lists empty
+  const int n = 2 * (len0 + len1);  // 64-key sub-steps
   const size_t rs = (size_t)H * D;
   const int hoff = h * D;
-  const int half = grp * kPPHalf;  // this group's 64 keys inside a tile
 
-  const int qrow = qt * 128 + wq * 32 + col;
-  const bool qin = qrow < nq;
+  const int qrow = qmine * 128 + wq * 32 + col;
+  const bool qin = qmine >= 0 && qrow < nq;
   const int qid = qin ? q_ids[qrow] : -1;
   const bool qvalid = qid >= 0;
 
@@ -306,58 +337,56 @@ fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   f32x16 sacc[2];
   bf16x8 pb[4];
 
-  // Scalar per-tile values are fetched one step ahead, during a softmax phase,
-  // and consumed before the next MFMA phase: an outstanding scalar load would
-  // force every LDS operand wait in the MFMA phase down to zero.
-  // kt_c / kt_n: key tiles t and t + 1; partial_c: tile t needs the mask.
-  int kt_c = n > 0 ? q_cols[beg] : 0;
-  int kt_n = n > 1 ? q_cols[beg + 1] : 0;
-  bool partial_c = n > 0 && tile_class_at(tile_class, (size_t)qt * nkt + kt_c) == 1;
+  // first key row of sub-step s; whether sub-step s needs the id mask for
+  // this group's tile (not a full tile: partial, or empty = all masked)
+  const auto tile_of = [&](int s) {
+    const int u = s >> 1;
+    return u < len0 ? lo0 + u : lo1 + (u - len0);
+  };
+  const auto k0_of = [&](int s) { return tile_of(s) * 128 + 64 * (s & 1); };
+  const auto needs_mask = [&](int s) {
+    return qmine < 0 || tile_class_at(tile_class, (size_t)qmine * nkt + tile_of(s)) != 2;
+  };
+  bool partial_c = n > 0 && needs_mask(0);
 
-  // This wave's share of the loads of one step: pieces 0-3 are K rows of tile
-  // ktk, pieces 4-7 V rows of tile ktv, all in this group's half.
-  // Every piece of this wave has row groups blk = wq + 4 j, whose swizzle
-  // (4 (lane / 16) + blk % 4 on the chunk) is the same for all four.
+  // Group A stages the K sub-tiles (and their ids, by wave 0), group B the V
+  // sub-tiles: 16 row groups over a group's four waves (row groups wq + 4 j,
+  // one swizzle for all four).
   const uint32_t group_bytes = (uint32_t)(4 * rs * 2);
   const uint32_t lane_off =
       (uint32_t)((((size_t)(lane >> 4) * rs + hoff) * 2) +
                  (((lane & 15) ^ (4 * (lane >> 4) + wq)) << 4));
-  const auto load_piece = [&](int j, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                              char* kdst, char* vdst) __attribute__((always_inline)) {
-    if (j < 4)
-      stage_piece(rk, lane_off, group_bytes, kdst + half, wq + 4 * j);
-    else
-      stage_piece(rv, lane_off, group_bytes, vdst + half, wq + 4 * (j - 4));
+  // rows row0 .. nkv - 1 of a K or V tensor (reads past them return zeros)
+  const auto rows = [&](const uint16_t* g, int row0) {
+    const uint64_t bytes = row0 < nkv ? (uint64_t)(nkv - row0) * rs * 2 : 0;
+    return raw_rsrc(g + (size_t)row0 * rs, bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes);
   };
-  const auto k_rsrc = [&](int kt) { return rows_rsrc(k, rs, kt * 128 + 64 * grp, nkv); };
-  const auto v_rsrc = [&](int kt) { return rows_rsrc(v, rs, kt * 128 + 64 * grp, nkv); };
-  const auto load_ids = [&](int ktk, char* kdst) __attribute__((always_inline)) {
-    if (wq == 0) stage_ids(kv_ids, ktk * 128 + 64 * grp, nkv, kdst + kPPTile + 256 * grp, lane);
+  const auto load_piece = [&](int j, u32x4_t r, char* dst) __attribute__((always_inline)) {
+    const int blk = wq + 4 * j;
+    dma_b128(r, lane_off + blk * group_bytes, lds_address(dst + blk * 1024));
   };
 
-  // MFMA phase: O^T += V^T P^T of the previous tile (V from vprev), then
-  // S^T = K Q^T of this tile (K from kcur), masked on partial tiles.  With no
-  // second MFMA wave on the SIMD, the LDS latency of the operand reads has to
-  // hide behind this wave's own MFMAs: the MFMAs go in batches of four, and
-  // the reads of batch b + 1 are issued right after the first MFMA of batch b
-  // (registers for two batches), pinned in that order by scheduling groups;
-  // `hook(b)` (this step's direct loads, or nothing) follows them.
+  // MFMA phase: O^T += V^T P^T of the previous sub-tile (V from vprev), then
+  // S^T = K Q^T of this one (K from kcur), masked unless the tile is full for
+  // this group.  With no second MFMA wave on the SIMD, the LDS latency of the
+  // operand reads has to hide behind this wave's own MFMAs: the MFMAs go in
+  // batches of four, and the reads of batch b + 1 are issued right after the
+  // first MFMA of batch b (registers for two batches), pinned in that order by
+  // scheduling groups.
   //   MFMA i <  16: PV, kb = i / 4, db = i % 4 (A = V^T slice, B = pb[kb])
   //   MFMA i >= 16: S,  kk = (i - 16) / 2, mb = (i - 16) % 2 (A = K rows, B = qf[kk])
-  // kind: 0 = scores only (first tile), 1 = PV only (after the last tile), 2 = both
-  const auto mfma_phase = [&](auto kind, const char* kcur, const char* vprev, bool partial,
-                              auto hook) __attribute__((always_inline)) {
+  // kind: 0 = scores only (first sub-tile), 1 = PV only (after the last), 2 = both
+  const auto mfma_phase = [&](auto kind, const char* kcur, const char* vprev, bool partial)
+                              __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
-    const char* vb = vprev + half;
-    const char* kb_ = kcur + half;
     const auto load_op = [&](int i) __attribute__((always_inline)) {
       if (i < 16) {
         const int kb = i >> 2, db = i & 3;
-        return join8(lds_tr4(vb, tr_at(tb, db, 0) + 4096 * kb),
-                     lds_tr4(vb, tr_at(tb, db, 1) + 4096 * kb));
+        return join8(lds_tr4(vprev, tr_at(tb, db, 0) + 4096 * kb),
+                     lds_tr4(vprev, tr_at(tb, db, 1) + 4096 * kb));
       }
       const int kk = (i - 16) >> 1, mb = (i - 16) & 1;
-      return lds_row8(kb_, row_at(rb, kk) + 8192 * mb);
+      return lds_row8(kcur, row_at(rb, kk) + 8192 * mb);
     };
     const auto do_mfma = [&](int i, bf16x8 a) __attribute__((always_inline)) {
       if (i < 16) {
@@ -393,13 +422,12 @@ fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         else
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
-      hook((b - first) >> 2);
 #pragma unroll
       for (int e = 1; e < 4; ++e) do_mfma(b + e, op[cur][e]);
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     }
     if (K != 1 && partial) {
-      const int32_t* il = (const int32_t*)(kcur + kPPTile) + 64 * grp;
+      const int32_t* il = (const int32_t*)(kcur + kPrSub);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -417,9 +445,7 @@ fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
 
-  // softmax phase: online softmax of the scores, P as bf16 MFMA operands;
-  // `hook(j)`, j = 0..7, places this step's direct loads between the exp blocks
-  const auto softmax_phase = [&](auto hook) __attribute__((always_inline)) {
+  const auto softmax_phase = [&]() __attribute__((always_inline)) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -450,24 +476,12 @@ fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
       pb[kb] = __builtin_bit_cast(bf16x8, w);
-      hook(2 * kb);
-      hook(2 * kb + 1);
     }
     // the results exist here: keeps the compiler from sinking the softmax
     // past the barrier that ends the phase, into the MFMA phase that uses it
     asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(lsum));
   };
 
-  // Group A runs, per key tile t, the MFMA phase t (PV of tile t - 1, scores
-  // of tile t) and then the softmax of tile t; group B the softmax of tile
-  // t - 1 and then the MFMA phase t, so the groups are one phase apart.  Each
-  // step has two barriers: a plain one between its phases (it only keeps the
-  // groups in step; no buffer changes hands there; the scheduling fences keep
-  // each phase's instructions on its side) and one after the wait for the
-  // step's loads (K of tile t + 1, V of tile t), which the next step reads.
-  // A barrier that only orders the waves: no wait for outstanding loads (each
-  // group waits for its own loads where it needs them), and no instruction or
-  // memory access crosses it.
   const auto barrier = []() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -475,135 +489,130 @@ fwd_bf16_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  int kt_nn = 0, partial_n = 0;
-  // next step's scalars: fetched at the start of a softmax phase ...
-  const auto fetch_next = [&](int t) __attribute__((always_inline)) {
-    kt_nn = t + 2 < n ? q_cols[beg + t + 2] : 0;
-    partial_n = t + 1 < n ? tile_class_at(tile_class, (size_t)qt * nkt + kt_n) == 1 : 0;
+  int partial_n = 0;
+  const auto fetch_next = [&](int s) __attribute__((always_inline)) {
+    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
   };
-  // ... and in registers by its end
   const auto land_next = [&]() __attribute__((always_inline)) {
-    asm volatile("" ::"s"(kt_nn), "s"(partial_n));
+    asm volatile("" ::"s"(partial_n));
   };
-  const auto rotate = [&]() __attribute__((always_inline)) {
-    kt_c = kt_n;
-    kt_n = kt_nn;
-    partial_c = partial_n;
-  };
-  const auto no_hook = [](int) {};
-  // K of tile t + 1 (the last step re-reads tile t into the unused buffer)
-  const auto ktk_of = [&](int t) { return t + 1 < n ? kt_n : kt_c; };
-  // MFMA phase t with this group's loads for step t + 1 (K of tile t + 1, V of
-  // tile t) between its MFMAs: each group issues its loads in its own MFMA
-  // phase, so the address unit sees the two groups' loads in alternate phases
-  const auto mfma_with_loads = [&](int t, auto kind, const char* kcur, char* knext,
-                                   const char* vprev, char* vcur) __attribute__((always_inline)) {
-    constexpr int K = decltype(kind)::value;
-    if (K != 1) {
-      const int ktk = ktk_of(t);
-      const auto rk = k_rsrc(ktk), rv = v_rsrc(kt_c);
-      load_ids(ktk, knext);
-      mfma_phase(kind, kcur, vprev, partial_c, [&](int b) __attribute__((always_inline)) {
-        if (K == 2) {
-          load_piece(b, rk, rv, knext, vcur);
-        } else {
-          load_piece(2 * b, rk, rv, knext, vcur);
-          load_piece(2 * b + 1, rk, rv, knext, vcur);
-        }
-      });
-    } else {
-      mfma_phase(kind, kcur, vprev, partial_c, no_hook);
+  // Three buffers each for K and V: sub-tile s sits in kb[s % 3] / vb[s % 3].
+  // Step s stages K(s + 2) (group A, during its MFMA phase) and V(s + 1)
+  // (group B, during its MFMA phase); each wave waits for its previous step's
+  // loads at the end of step s + 1, so a load has two steps to land.  Past the
+  // last sub-tile the loads re-read sub-tile n - 1 into the free buffer, which
+  // keeps the per-step load count (and so the partial waits) fixed.
+  const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
+  // Each wave of group A stages 16 of the sub-tile's 64 key ids (one load
+  // with 16 active lanes), so every wave of a group issues the same number of
+  // loads per step.
+  const auto load_ids = [&](int k0, char* kdst) __attribute__((always_inline)) {
+    if ((lane >> 4) == wq) {
+      const int i = k0 + lane;
+      dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kPrSub));
     }
   };
-  // group A: MFMA phase t (its loads land by the end of the step), softmax t
-  const auto step_a = [&](int t, auto kind, const char* kcur, char* knext, const char* vprev,
-                          char* vcur) __attribute__((always_inline)) {
+  // wait until only this step's loads are outstanding (loads finish in order):
+  // group A issues 5 per step (4 K pieces + ids), group B 4 (V pieces)
+  const auto wait_prev_a = [&](auto kind) __attribute__((always_inline)) {
+    if (decltype(kind)::value == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+  };
+  const auto wait_prev_b = [&](auto kind) __attribute__((always_inline)) {
+    if (decltype(kind)::value == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  };
+  // Each group issues its direct loads at the start of its softmax phase: the
+  // other group is then in its MFMA phase, reading LDS at full rate, and loads
+  // issued by an MFMA-phase wave stalled it (measured).
+  // group A: MFMA phase s, then loads of K(s + 2) and softmax s
+  const auto step_a = [&](int s, auto kind, const char* kcur, const char* vprev, char* kload)
+                          __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
-    mfma_with_loads(t, kind, kcur, knext, vprev, vcur);
+    mfma_phase(kind, kcur, vprev, partial_c);
     barrier();
-    fetch_next(t);
-    if (K != 1) softmax_phase(no_hook);
+    if (K != 1) {
+      const int k0n = k0_of(last_sub(s + 2));
+      const auto rk = rows(k, k0n);
+      load_ids(k0n, kload);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_piece(j, rk, kload);
+    }
+    fetch_next(s);
+    if (K != 1) softmax_phase();
     land_next();
-    rotate();
-    wait_vmem();
+    partial_c = partial_n;
+    wait_prev_a(kind);
     barrier();
   };
-  // group B: softmax t - 1 (then its loads of the previous step have landed),
-  // MFMA phase t
-  const auto step_b = [&](int t, auto kind, const char* kcur, char* knext, const char* vprev,
-                          char* vcur) __attribute__((always_inline)) {
+  // group B: loads of V(s + 1) and softmax s - 1, then MFMA phase s
+  const auto step_b = [&](int s, auto kind, const char* kcur, const char* vprev, char* vload)
+                          __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
-    fetch_next(t);
-    if (K != 0) softmax_phase(no_hook);
+    if (K != 1) {
+      const auto rv = rows(v, k0_of(last_sub(s + 1)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_piece(j, rv, vload);
+    }
+    fetch_next(s);
+    if (K != 0) softmax_phase();
     land_next();
-    wait_vmem();
     barrier();
-    mfma_with_loads(t, kind, kcur, knext, vprev, vcur);
-    rotate();
+    mfma_phase(kind, kcur, vprev, partial_c);
+    partial_c = partial_n;
+    wait_prev_b(kind);
     barrier();
   };
   using First = std::integral_constant<int, 0>;
   using Last = std::integral_constant<int, 1>;
   using Mid = std::integral_constant<int, 2>;
+  // prologue: K(0) -> kb0, K(1) -> kb1 (group A), V(0) -> vb0 (group B)
   if (n > 0) {
-    load_ids(kt_c, kb0);
-    const auto rk = k_rsrc(kt_c);
+    if (grp == 0) {
+      const int k00 = k0_of(0), k01 = k0_of(last_sub(1));
+      const auto r0 = rows(k, k00), r1 = rows(k, k01);
+      load_ids(k00, kb0);
+      load_ids(k01, kb1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_piece(j, rk, rk, kb0, vb0);
+      for (int j = 0; j < 4; ++j) {
+        load_piece(j, r0, kb0);
+        load_piece(j, r1, kb1);
+      }
+    } else {
+      const auto r0 = rows(v, k0_of(0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_piece(j, r0, vb0);
+    }
   }
   wait_vmem();
   __syncthreads();
-  // steps t = 0 .. n: the first computes scores only, the last PV only; the
-  // middle ones alternate the buffer pairs
-  char* const vlast = (n & 1) ? vb0 : vb1;  // V of tile n - 1
-  if (grp == 0) {
-    if (n > 0) {
-      step_a(0, First{}, kb0, kb1, vb1, vb0);
-      for (int t = 1; t < n; t += 2) {
-        step_a(t, Mid{}, kb1, kb0, vb0, vb1);
-        if (t + 1 < n) step_a(t + 1, Mid{}, kb0, kb1, vb1, vb0);
+  if (n > 0) {
+    // buffers of step s (r = s % 3): kcur kb[r], vprev vb[(r + 2) % 3],
+    // K load into kb[(r + 2) % 3], V load into vb[(r + 1) % 3]
+    char* const vlast = (n - 1) % 3 == 0 ? vb0 : (n - 1) % 3 == 1 ? vb1 : vb2;
+    if (grp == 0) {
+      step_a(0, First{}, kb0, vb2, kb2);
+      for (int s = 1; s < n; s += 3) {
+        step_a(s, Mid{}, kb1, vb0, kb0);
+        if (s + 1 < n) step_a(s + 1, Mid{}, kb2, vb1, kb1);
+        if (s + 2 < n) step_a(s + 2, Mid{}, kb0, vb2, kb2);
       }
-      step_a(n, Last{}, kb0, kb1, vlast, vb0);
-    }
-  } else {
-    if (n > 0) {
-      step_b(0, First{}, kb0, kb1, vb1, vb0);
-      for (int t = 1; t < n; t += 2) {
-        step_b(t, Mid{}, kb1, kb0, vb0, vb1);
-        if (t + 1 < n) step_b(t + 1, Mid{}, kb0, kb1, vb1, vb0);
+      step_a(n, Last{}, kb0, vlast, kb2);
+    } else {
+      step_b(0, First{}, kb0, vb2, vb1);
+      for (int s = 1; s < n; s += 3) {
+        step_b(s, Mid{}, kb1, vb0, vb2);
+        if (s + 1 < n) step_b(s + 1, Mid{}, kb2, vb1, vb0);
+        if (s + 2 < n) step_b(s + 2, Mid{}, kb0, vb2, vb1);
       }
-      step_b(n, Last{}, kb0, kb1, vlast, vb0);
+      step_b(n, Last{}, kb0, vlast, vb0);
     }
   }
 
-  // merge: group B hands (O, running max, partial sum) to its group-A partner,
-  // whose lanes hold the same (query, column) elements
-  static_assert((16 * kDB + 2) * 64 * 4 <= kPPTile, "one wave's partial fits a buffer");
-  float* xo = (float*)(wq == 0 ? kb0 : wq == 1 ? kb1 : wq == 2 ? vb0 : vb1);
-  if (grp == 1) {
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xo[(16 * db + j) * 64 + lane] = oacc[db][j];
-    xo[16 * kDB * 64 + lane] = m;
-    xo[(16 * kDB + 1) * 64 + lane] = lsum;
-  }
-  __syncthreads();
-  if (grp == 1) return;
-  {
-    const float mb_ = xo[16 * kDB * 64 + lane];
-    const float lb = xo[(16 * kDB + 1) * 64 + lane];
-    const float mn = fmaxf(m, mb_);
-    const float ca = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-    const float cb = mb_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb_ - mn);
-    lsum = lsum * ca + lb * cb;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        oacc[db][j] = oacc[db][j] * ca + xo[(16 * db + j) * 64 + lane] * cb;
-    m = mn;
-  }
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const bool any = ltot > 0.f;
   const float inv = any ? 1.f / ltot : 0.f;
@@ -734,7 +743,8 @@ extern "C" int32_t attn_packed_fwd(int32_t dtype, int32_t nq, int32_t nkv, int32
   if (dtype == PA_BF16) {
     const float s2 = scale * pa::kLog2e;
     if (head_dim == 128)
-      hipLaunchKernelGGL(fwd_bf16_pp_kernel<128>, grid, dim3(512), 0, s, (const uint16_t*)q,
+      hipLaunchKernelGGL(fwd_bf16_pair_kernel<128>, dim3((mask->nq_tiles + 1) / 2 * heads),
+                         dim3(512), 0, s, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, q_seq_id, kv_seq_id, nq, nkv,
                          heads, s2, mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,
                          mask->nkv_tiles, (uint16_t*)o, lse);
