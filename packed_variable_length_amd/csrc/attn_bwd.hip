@@ -28,6 +28,8 @@
 // (K^T, Q^T, dO^T) are read with ds_read_b64_tr_b16 from the same row-major
 // tiles (see pa_tile.h).
 #include <math.h>
+#include <type_traits>
+#include <limits.h>
 
 #include "pa_common.h"
 #include "pa_tile.h"
@@ -212,6 +214,361 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int s = 0; s < nsub; s += 2) {
     step(s, st0, st1);
     if (s + 1 < nsub) step(s + 1, st1, st0);
+  }
+  if (qin) {
+    uint16_t* op = dq + (size_t)qrow * rs + hoff;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale);
+        pk[1] = pack_bf16x2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+        *(u32x2*)(op + db * 32 + 8 * g + 4 * hi) = pk;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 dq, paired
+// 128-wide heads: a workgroup of 8 waves per pair of query tiles (positions 2w
+// and 2w + 1 of the longest-first order), one per wave group, like the
+// forward's paired kernel.  Both groups walk the same 64-key sub-tiles one
+// phase apart: group A runs the MFMA phase of sub-tile s (dQ^T += K^T dS^T of
+// s - 1, then S^T = K Q^T and dP^T = V dO^T of s) and then the VALU phase of
+// s (P = exp2(S s2 - LSE2), dS = P (dP - Delta)); group B the VALU phase of
+// s - 1 and then the MFMA phase of s.  K(s) is read in two steps (S of s,
+// dQ of s), so K and V each get four LDS buffers; sub-tiles are staged two
+// steps ahead by the group in its VALU phase (A: K and ids, B: V).
+constexpr int kDqSub = 64 * kRowBytes;  // one 64-key sub-tile (16 KB)
+
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                    const float* __restrict__ delta, const float* __restrict__ lse2,
+                    const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
+                    int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
+                    const uint8_t* __restrict__ tile_class, const int32_t* __restrict__ q_ptr,
+                    const int32_t* __restrict__ q_cols, const int32_t* __restrict__ q_order,
+                    int32_t nkt, uint16_t* __restrict__ dq) {
+  static_assert(D == 128, "the paired dQ kernel is laid out for 128-wide heads");
+  constexpr int kDB = D / 32, kKK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char kb0[kDqSub + 256];
+  __shared__ __attribute__((aligned(1024))) char kb1[kDqSub + 256];
+  __shared__ __attribute__((aligned(1024))) char kb2[kDqSub + 256];
+  __shared__ __attribute__((aligned(1024))) char kb3[kDqSub + 256];
+  __shared__ __attribute__((aligned(1024))) char vb0[kDqSub];
+  __shared__ __attribute__((aligned(1024))) char vb1[kDqSub];
+  __shared__ __attribute__((aligned(1024))) char vb2[kDqSub];
+  __shared__ __attribute__((aligned(1024))) char vb3[kDqSub];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const int hi = lane >> 5, col = lane & 31;
+  const int grp = wv >> 2, wq = wv & 3;
+  const int nqt = (nq + 127) / 128;
+  int work, h;
+  block_work(blockIdx.x, H, (nqt + 1) / 2, &work, &h);
+  const int qpair[2] = {q_order[2 * work], 2 * work + 1 < nqt ? q_order[2 * work + 1] : -1};
+  const int qmine = qpair[grp];  // -1: no tile (odd tile count), no rows, all masked
+  // the key walk: each tile's key-tile range [first, last] of its list; one
+  // segment when the two overlap or touch, else both one after the other
+  int first[2], last[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    first[g] = INT_MAX;
+    last[g] = -1;
+    if (qpair[g] >= 0 && q_ptr[qpair[g] + 1] > q_ptr[qpair[g]]) {
+      first[g] = q_cols[q_ptr[qpair[g]]];
+      last[g] = q_cols[q_ptr[qpair[g] + 1] - 1];
+    }
+  }
+  int lo0, len0, lo1 = 0, len1 = 0;
+  if (last[1] < 0 || (last[0] >= 0 && first[1] <= last[0] + 1 && first[0] <= last[1] + 1)) {
+    lo0 = min(first[0], first[1]);
+    len0 = max(last[0], last[1]) - lo0 + 1;
+  } else if (last[0] < 0) {
+    lo0 = first[1];
+    len0 = last[1] - first[1] + 1;
+  } else {
+    const int g0 = first[0] <= first[1] ? 0 : 1;
+    lo0 = first[g0];
+    len0 = last[g0] - first[g0] + 1;
+    lo1 = first[1 - g0];
+    len1 = last[1 - g0] - first[1 - g0] + 1;
+  }
+  if (len0 < 0) len0 = 0;
+  const int n = 2 * (len0 + len1);  // 64-key sub-steps
+  const size_t rs = (size_t)H * D;
+  const int hoff = h * D;
+
+  const int qrow = qmine * 128 + wq * 32 + col;
+  const bool qin = qmine >= 0 && qrow < nq;
+  const int qc = qin ? qrow : nq - 1;
+  const int qid = qin ? q_ids[qrow] : -1;
+  const bool qvalid = qid >= 0;
+  const float nl2 = -lse2[(size_t)h * nq + qc];  // -inf on rows without a key: P = 0
+  const float dlt = delta[(size_t)h * nq + qc];
+
+  bf16x8 qf[kKK], df[kKK];
+  {
+    const uint16_t* qp = q + (size_t)qc * rs + hoff + 8 * hi;
+    const uint16_t* dp = dout + (size_t)qc * rs + hoff + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+      df[kk] = *(const bf16x8*)(dp + 16 * kk);
+    }
+  }
+  const int rb = row_base(lane), tb = tr_base(lane);
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  f32x16 st[2], dpt[2];  // S^T, dP^T of the current sub-tile (keys 32mb + ...)
+  bf16x8 dsb[4];         // dS^T of the previous one, as MFMA operands (16 keys each)
+
+  const auto tile_of = [&](int s) {
+    const int u = s >> 1;
+    return u < len0 ? lo0 + u : lo1 + (u - len0);
+  };
+  const auto k0_of = [&](int s) { return tile_of(s) * 128 + 64 * (s & 1); };
+  const auto needs_mask = [&](int s) {
+    return qmine < 0 || tile_class_at(tile_class, (size_t)qmine * nkt + tile_of(s)) != 2;
+  };
+  bool partial_c = n > 0 && needs_mask(0);
+
+  const uint32_t group_bytes = (uint32_t)(4 * rs * 2);
+  const uint32_t lane_off =
+      (uint32_t)((((size_t)(lane >> 4) * rs + hoff) * 2) +
+                 (((lane & 15) ^ (4 * (lane >> 4) + wq)) << 4));
+  const auto rows = [&](const uint16_t* g, int row0) {
+    const uint64_t bytes = row0 < nkv ? (uint64_t)(nkv - row0) * rs * 2 : 0;
+    return raw_rsrc(g + (size_t)row0 * rs, bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes);
+  };
+  const auto load_piece = [&](int j, u32x4_t r, char* dst) __attribute__((always_inline)) {
+    const int blk = wq + 4 * j;
+    dma_b128(r, lane_off + blk * group_bytes, lds_address(dst + blk * 1024));
+  };
+  const auto load_ids = [&](int k0, char* kdst) __attribute__((always_inline)) {
+    // the lane index recomputed here (mbcnt) rather than kept live across the loop
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if ((ln >> 4) == wq) {
+      const int i = k0 + ln;
+      dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kDqSub));
+    }
+  };
+
+  // MFMA phase: dQ^T += K^T dS^T of the previous sub-tile (K^T read transposed
+  // from kprev), then S^T = K Q^T and dP^T = V dO^T of this one (kcur, vcur),
+  // masked unless the tile is full for this group; MFMAs in batches of four
+  // with the next batch's operand reads in flight.
+  //   MFMA i <  16: dQ, kb = i / 4, db = i % 4 (A = K^T slice, B = dsb[kb])
+  //   MFMA i >= 16: j = i - 16, kk = j / 4, mb = j % 2, V rows if j % 4 >= 2 (S/dP)
+  // kind: 0 = S/dP only (first sub-tile), 1 = dQ only (after the last), 2 = both
+  const auto mfma_phase = [&](auto kind, const char* kcur, const char* kprev, const char* vcur,
+                              bool partial) __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    const auto load_op = [&](int i) __attribute__((always_inline)) {
+      if (i < 16) {
+        const int kb = i >> 2, db = i & 3;
+        return join8(lds_tr4(kprev, tr_at(tb, db, 0) + 4096 * kb),
+                     lds_tr4(kprev, tr_at(tb, db, 1) + 4096 * kb));
+      }
+      const int j = i - 16, kk = j >> 2, mb = j & 1;
+      return lds_row8((j & 2) ? vcur : kcur, row_at(rb, kk) + 8192 * mb);
+    };
+    const auto do_mfma = [&](int i, bf16x8 a) __attribute__((always_inline)) {
+      if (i < 16) {
+        const int kb = i >> 2, db = i & 3;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[kb], acc[db], 0, 0, 0);
+      } else {
+        // the first contraction step starts from zero: S^T and dP^T are not
+        // live before it (registers for the dQ part of the phase)
+        const int j = i - 16, kk = j >> 2, mb = j & 1;
+        const f32x16 zero = {};
+        if (j & 2)
+          dpt[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[kk], kk ? dpt[mb] : zero, 0, 0, 0);
+        else
+          st[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk ? st[mb] : zero, 0, 0, 0);
+      }
+    };
+    constexpr int first_i = K == 0 ? 16 : 0, last_i = K == 1 ? 16 : 48;
+    bf16x8 op[2][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) op[0][e] = load_op(first_i + e);
+    if (first_i < 16)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int b = first_i; b < last_i; b += 4) {
+      const int cur = ((b - first_i) >> 2) & 1;
+      do_mfma(b, op[cur][0]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (b + 4 < last_i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[cur ^ 1][e] = load_op(b + 4 + e);
+        if (b + 4 < 16)
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+#pragma unroll
+      for (int e = 1; e < 4; ++e) do_mfma(b + e, op[cur][e]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
+    if (K != 1 && partial) {
+      const int32_t* il = (const int32_t*)(kcur + kDqSub);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int4 t4 = *(const int4*)(il + mb * 32 + 8 * g + 4 * hi);  // -1 past the end
+          st[mb][4 * g + 0] = (qvalid & (t4.x == qid)) ? st[mb][4 * g + 0] : -INFINITY;
+          st[mb][4 * g + 1] = (qvalid & (t4.y == qid)) ? st[mb][4 * g + 1] : -INFINITY;
+          st[mb][4 * g + 2] = (qvalid & (t4.z == qid)) ? st[mb][4 * g + 2] : -INFINITY;
+          st[mb][4 * g + 3] = (qvalid & (t4.w == qid)) ? st[mb][4 * g + 3] : -INFINITY;
+        }
+    }
+  };
+
+  // VALU phase: P = exp2(S s2 - LSE2) (0 on masked scores), dS = P (dP - Delta)
+  const auto valu_phase = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int mb = kb >> 1, b0 = (kb & 1) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = b0 + 2 * e;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(st[mb][j], s2, nl2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(st[mb][j + 1], s2, nl2));
+        w[e] = pack_bf16x2(p0 * (dpt[mb][j] - dlt), p1 * (dpt[mb][j + 1] - dlt));
+      }
+      dsb[kb] = __builtin_bit_cast(bf16x8, w);
+    }
+    // the results exist here: keeps the compiler from sinking this phase past
+    // the barrier that ends it, into the MFMA phase that uses it
+    asm volatile("" ::"v"(dsb[0]), "v"(dsb[1]), "v"(dsb[2]), "v"(dsb[3]));
+  };
+
+  const auto barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int partial_n = 0;
+  const auto fetch_next = [&](int s) __attribute__((always_inline)) {
+    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
+  };
+  const auto land_next = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::"s"(partial_n));
+  };
+  const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
+  // Loads of step s: K(s + 2) and its ids (group A, 5 per wave), V(s + 2)
+  // (group B, 4 per wave), issued at the start of the group's VALU phase and
+  // waited for at the end of step s + 1 (loads finish in order).
+  const auto wait_prev_a = [&](auto kind) __attribute__((always_inline)) {
+    if (decltype(kind)::value == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+  };
+  const auto wait_prev_b = [&](auto kind) __attribute__((always_inline)) {
+    if (decltype(kind)::value == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  };
+  const auto step_a = [&](int s, auto kind, const char* kcur, const char* kprev,
+                          const char* vcur, char* kload) __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    mfma_phase(kind, kcur, kprev, vcur, partial_c);
+    barrier();
+    if (K != 1) {
+      const int k0n = k0_of(last_sub(s + 2));
+      const auto rk = rows(k, k0n);
+      load_ids(k0n, kload);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_piece(j, rk, kload);
+    }
+    fetch_next(s);
+    if (K != 1) valu_phase();
+    land_next();
+    partial_c = partial_n;
+    wait_prev_a(kind);
+    barrier();
+  };
+  const auto step_b = [&](int s, auto kind, const char* kcur, const char* kprev,
+                          const char* vcur, char* vload) __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    if (K != 1) {
+      const auto rv = rows(v, k0_of(last_sub(s + 2)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_piece(j, rv, vload);
+    }
+    fetch_next(s);
+    if (K != 0) valu_phase();
+    land_next();
+    barrier();
+    mfma_phase(kind, kcur, kprev, vcur, partial_c);
+    partial_c = partial_n;
+    wait_prev_b(kind);
+    barrier();
+  };
+  using First = std::integral_constant<int, 0>;
+  using Last = std::integral_constant<int, 1>;
+  using Mid = std::integral_constant<int, 2>;
+  // prologue: K(0), K(1) (group A), V(0), V(1) (group B)
+  if (n > 0) {
+    const int k00 = k0_of(0), k01 = k0_of(last_sub(1));
+    if (grp == 0) {
+      const auto r0 = rows(k, k00), r1 = rows(k, k01);
+      load_ids(k00, kb0);
+      load_ids(k01, kb1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        load_piece(j, r0, kb0);
+        load_piece(j, r1, kb1);
+      }
+    } else {
+      const auto r0 = rows(v, k00), r1 = rows(v, k01);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        load_piece(j, r0, vb0);
+        load_piece(j, r1, vb1);
+      }
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (n > 0) {
+    // step s (r = s % 4): kcur kb[r], kprev kb[(r + 3) % 4], vcur vb[r],
+    // loads into kb[(r + 2) % 4] / vb[(r + 2) % 4]
+    const int rl = (n - 1) & 3;
+    const char* const klast = rl == 0 ? kb0 : rl == 1 ? kb1 : rl == 2 ? kb2 : kb3;
+    if (grp == 0) {
+      step_a(0, First{}, kb0, kb3, vb0, kb2);
+      for (int s = 1; s < n; s += 4) {
+        step_a(s, Mid{}, kb1, kb0, vb1, kb3);
+        if (s + 1 < n) step_a(s + 1, Mid{}, kb2, kb1, vb2, kb0);
+        if (s + 2 < n) step_a(s + 2, Mid{}, kb3, kb2, vb3, kb1);
+        if (s + 3 < n) step_a(s + 3, Mid{}, kb0, kb3, vb0, kb2);
+      }
+      step_a(n, Last{}, kb0, klast, vb0, kb2);
+    } else {
+      step_b(0, First{}, kb0, kb3, vb0, vb2);
+      for (int s = 1; s < n; s += 4) {
+        step_b(s, Mid{}, kb1, kb0, vb1, vb3);
+        if (s + 1 < n) step_b(s + 1, Mid{}, kb2, kb1, vb2, vb0);
+        if (s + 2 < n) step_b(s + 2, Mid{}, kb3, kb2, vb3, vb1);
+        if (s + 3 < n) step_b(s + 3, Mid{}, kb0, kb3, vb0, vb2);
+      }
+      step_b(n, Last{}, kb0, klast, vb0, vb2);
+    }
   }
   if (qin) {
     uint16_t* op = dq + (size_t)qrow * rs + hoff;
@@ -548,6 +905,7 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                   const int32_t* kv_seq_id, const pa_block_mask* mask, void* dq, void* dk,
                   void* dv, float* ws, hipStream_t s) {
   const dim3 gq(mask ? mask->nq_tiles * heads : 1), gk(mask ? mask->nkv_tiles * heads : 1);
+  const dim3 gq2(mask ? (mask->nq_tiles + 1) / 2 * heads : 1);  // pairs of query tiles
   const float s2 = scale * pa::kLog2e;
   const bool bf = dtype == PA_BF16;
   float* delta = ws;
@@ -557,7 +915,13 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
     if (bf) launch_preprocess<uint16_t, D>(o, dout, lse, nq, heads, delta, lse2, s);             \
     else launch_preprocess<float, D>(o, dout, lse, nq, heads, delta, lse2, s);                   \
   } else if (stage == 1) {                                                                       \
-    if (bf)                                                                                      \
+    if (bf && D == 128)                                                                          \
+      hipLaunchKernelGGL(dq_bf16_pair_kernel<128>, gq2, dim3(512), 0, s, (const uint16_t*)q,     \
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
+                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
+                         mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,             \
+                         mask->nkv_tiles, (uint16_t*)dq);                                        \
+    else if (bf)                                                                                 \
       hipLaunchKernelGGL(dq_bf16_kernel<D>, gq, dim3(256), 0, s, (const uint16_t*)q,             \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
                          lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \

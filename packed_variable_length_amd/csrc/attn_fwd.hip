@@ -214,36 +214,6 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// Direct global->LDS loads issued from inline assembly.  The compiler does
-// not see these LDS writes, so it cannot answer them with conservative
-// vmcnt(0) waits in front of unrelated LDS reads (it did with the builtins
-// once three buffers of each kind were in flight); every use is ordered by
-// explicit vmcnt waits and barriers instead.  A kernel that uses them issues
-// no other LDS-DMA (they set M0 themselves).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// raw buffer descriptor over `bytes` bytes from `base` (range-checked loads)
-__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-
-// 16 bytes per lane from rsrc at byte offset voff to LDS (lane i at lds + 16 i)
-__device__ __forceinline__ void dma_b128(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
-}
-
-// 4 bytes per lane from the lane's address to LDS (lane i at lds + 4 i)
-__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               ::"v"(src), "s"(lds) : "memory");
-}
-
 // Paired ping-pong variant: a workgroup of 8 waves per PAIR of query tiles,
 // the tiles at positions 2w and 2w + 1 of the longest-first order (equal or
 // nearly equal key lists: for contiguous segments, two tiles of one segment).
