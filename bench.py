@@ -414,8 +414,8 @@ def main():
     kernels = {n: stage_ms[n] for n in FLOPS_PER_PAIR}
     dom = max(kernels, key=kernels.get)
     achieved = FLOPS_PER_PAIR[dom] * d * pairs * H / (kernels[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_bf16_kernel<128>",
-                                            "bwd_dq": "dq_bf16_kernel<128>",
+    roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_bf16_pair_kernel<128>",
+                                            "bwd_dq": "dq_bf16_pair_kernel<128>",
                                             "bwd_dkdv": "dkdv_bf16_kernel<128>"}[dom],
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
