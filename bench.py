@@ -416,7 +416,7 @@ def main():
     achieved = FLOPS_PER_PAIR[dom] * d * pairs * H / (kernels[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_bf16_pair_kernel<128>",
                                             "bwd_dq": "dq_bf16_pair_kernel<128>",
-                                            "bwd_dkdv": "dkdv_bf16_kernel<128>"}[dom],
+                                            "bwd_dkdv": "dkdv_bf16_split_kernel<128>"}[dom],
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom, spec.name),

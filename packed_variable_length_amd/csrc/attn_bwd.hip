@@ -746,6 +746,399 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
+// ------------------------------------------------------------------ bf16 dk, dv, split waves
+// 128-wide heads: a workgroup of 8 waves per 128-key tile; waves w and w + 4
+// (one SIMD) share keys 32w .. 32w + 31 and split the work: the P wave holds K
+// and the dV accumulator (S = Q K^T, P = exp2(S s2 - LSE2), dV^T += dO^T P),
+// the D wave holds V and the dK accumulator (dP = dO V^T, dS = P (dP - Delta),
+// dK^T += Q^T dS), with P handed over through LDS.  Each wave thus carries
+// half of the one-wave kernel's registers (room to keep its operand reads
+// ahead of its MFMAs), and the two alternate one phase apart per 64-query
+// sub-step s:
+//   phase X: P wave MFMAs (dV of s - 1, S of s); D wave VALU (dS of s - 1)
+//   phase Y: P wave VALU (P of s, into LDS);     D wave MFMAs (dK of s - 1, dP of s)
+// so each SIMD holds one MFMA wave and one VALU wave at a time.  Sub-tile s
+// (Q, dO, ids, LSE2, Delta) is read from phase X of s to phase Y of s + 1: four
+// LDS stages, staged two steps ahead by direct loads from inline assembly.  The
+// 32 row groups of a sub-tile are spread over all eight waves, and each wave
+// issues its loads one at a time between MFMAs or VALU work: a burst of direct
+// loads at a phase start stalls the issuing waves for hundreds of cycles.  A
+// wave's VALU phase also reads the first two operand batches of its next MFMA
+// phase, so that phase starts on MFMAs, not on LDS latency.
+constexpr int kSpSub = 64 * kRowBytes;                // one 64-query tile (16 KB)
+constexpr int kSpStage = 2 * kSpSub + 3 * 256;        // Q, dO, ids, LSE2, Delta
+constexpr int kSpIds = 2 * kSpSub, kSpLse = kSpIds + 256, kSpDelta = kSpLse + 256;
+
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                       const float* __restrict__ delta, const float* __restrict__ lse2,
+                       const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
+                       int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
+                       const uint8_t* __restrict__ tile_class,
+                       const int32_t* __restrict__ kv_ptr, const int32_t* __restrict__ kv_rows,
+                       const int32_t* __restrict__ kv_order, int32_t nkt,
+                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  static_assert(D == 128, "the split dK/dV kernel is laid out for 128-wide heads");
+  constexpr int kDB = D / 32, kKK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char st0[kSpStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kSpStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kSpStage];
+  __shared__ __attribute__((aligned(1024))) char st3[kSpStage];
+  __shared__ __attribute__((aligned(1024))) char xch[4 * 4096];  // P, per key block
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const int hi = lane >> 5, col = lane & 31;
+  const int grp = wv >> 2, wq = wv & 3;  // grp 0: P wave, 1: D wave
+  int work, h;
+  block_work(blockIdx.x, H, nkt, &work, &h);
+  const int kt = kv_order[work];
+  const int beg = kv_ptr[kt];
+  const int n = 2 * (kv_ptr[kt + 1] - beg);  // 64-query sub-steps
+  const size_t rs = (size_t)H * D;
+  const int hoff = h * D;
+
+  const int krow = kt * 128 + wq * 32 + col;
+  const bool kin = krow < nkv;
+  const int kc = kin ? krow : nkv - 1;
+  const int kid = kin ? kv_ids[krow] : -1;
+  const bool kvalid = kid >= 0;
+
+  bf16x8 kvf[kKK];  // K rows (P wave) or V rows (D wave) of this lane's key
+  {
+    const uint16_t* src = (grp == 0 ? k : v) + (size_t)kc * rs + hoff + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) kvf[kk] = *(const bf16x8*)(src + 16 * kk);
+  }
+  const int rb = row_base(lane), tb = tr_base(lane);
+  f32x16 gacc[kDB];  // dV^T (P wave) or dK^T (D wave)
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) gacc[db][j] = 0.f;
+  f32x16 sc[2];  // S (P wave) or dP (D wave) of the current sub-tile
+  bf16x8 ob[4];  // P (P wave) or dS (D wave) as MFMA operands, 16 queries each
+  char* const xb = xch + wq * 4096;
+
+  // per-step scalars, fetched a step ahead in a VALU phase (an outstanding
+  // scalar load would force every LDS operand wait of an MFMA phase to zero)
+  const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
+  const auto qt_of = [&](int s) { return kv_rows[beg + (last_sub(s) >> 1)]; };
+  const auto q0_of = [&](int s, int qt) { return qt * 128 + 64 * (last_sub(s) & 1); };
+  const auto needs_mask = [&](int s) {
+    return tile_class_at(tile_class, (size_t)qt_of(s) * nkt + kt) != 2;
+  };
+  int qt_l = n > 0 ? qt_of(2) : 0;  // query tile of the sub-tile this step loads
+  bool partial_c = n > 0 && needs_mask(0);
+  int qt_nl = 0, partial_n = 0;
+  const auto fetch_next = [&](int s) __attribute__((always_inline)) {
+    qt_nl = qt_of(s + 3);
+    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
+  };
+  const auto land_next = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::"s"(qt_nl), "s"(partial_n));
+  };
+  const auto rotate = [&]() __attribute__((always_inline)) {
+    qt_l = qt_nl;
+    partial_c = partial_n;
+  };
+
+  // direct loads: 16 row groups of a 64-row tile over a group's four waves
+  const uint32_t group_bytes = (uint32_t)(4 * rs * 2);
+  const uint32_t lane_off =
+      (uint32_t)((((size_t)(lane >> 4) * rs + hoff) * 2) +
+                 (((lane & 15) ^ (4 * (lane >> 4) + wq)) << 4));
+  const auto rows = [&](const uint16_t* g, int row0) {
+    const uint64_t bytes = row0 < nq ? (uint64_t)(nq - row0) * rs * 2 : 0;
+    return raw_rsrc(g + (size_t)row0 * rs, bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes);
+  };
+  // every wave stages 4 of a sub-tile's 32 row groups (2 of Q, 2 of dO): row
+  // groups wq + 4 (2 grp + j) of each, piece j in the step's phase j, so the
+  // direct loads of a step spread over all eight waves and both phases
+  const auto load_one = [&](int t, int j, int q0, char* stage) __attribute__((always_inline)) {
+    const int blk = wq + 4 * (2 * grp + j);
+    dma_b128(rows(t ? dout : q, q0), lane_off + blk * group_bytes,
+             lds_address(stage + t * kSpSub + blk * 1024));
+  };
+  const auto load_piece = [&](int j, int q0, char* stage) __attribute__((always_inline)) {
+    load_one(0, j, q0, stage);
+    load_one(1, j, q0, stage);
+  };
+  // D wave wq stages the ids (0), LSE2 (1) or Delta (2, and again 3) of 64 queries
+  // (so each D wave issues 5 loads per step, each P wave 4)
+  const auto load_words = [&](int q0, char* stage) __attribute__((always_inline)) {
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int i = q0 + ln;
+    const void* src;
+    if (wq == 0)
+      src = i < nq ? q_ids + i : &kNoId;
+    else
+      src = (wq == 1 ? lse2 : delta) + (size_t)h * nq + min(i, nq - 1);
+    dma_b32(src, lds_address(stage + (wq == 0 ? kSpIds : wq == 1 ? kSpLse : kSpDelta)));
+  };
+
+  // MFMA phase: gacc += tsrc^T ob over the previous sub-tile (dV^T += dO^T P or
+  // dK^T += Q^T dS; tsrc read transposed), then sc = rsrc K^T / rsrc V^T over
+  // this one (rsrc = Q or dO rows), in batches of four MFMAs with the next
+  // batch's operand reads in flight.
+  //   MFMA i <  16: kb = i / 4, db = i % 4 (A = tsrc^T slice, B = ob[kb])
+  //   MFMA i >= 16: j = i - 16, kk = j / 2, mb = j % 2 (A = rsrc rows, B = kvf[kk])
+  // kind: 0 = rows part only (first sub-tile), 1 = transposed part only, 2 = both
+  const auto load_op = [&](int i, const char* tsrc, const char* rsrc) __attribute__((always_inline)) {
+    if (i < 16) {
+      const int kb = i >> 2, db = i & 3;
+      return join8(lds_tr4(tsrc, tr_at(tb, db, 0) + 4096 * kb),
+                   lds_tr4(tsrc, tr_at(tb, db, 1) + 4096 * kb));
+    }
+    const int j = i - 16, kk = j >> 1, mb = j & 1;
+    return lds_row8(rsrc, row_at(rb, kk) + 8192 * mb);
+  };
+  bf16x8 op[3][4];  // operand ring: two batches of reads in flight
+  // the first two batches of an MFMA phase, read during the wave's VALU phase
+  const auto prefetch = [&](auto kind, const char* tsrc, const char* rsrc)
+                            __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    constexpr int first_i = K == 0 ? 16 : 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) op[e >> 2][e & 3] = load_op(first_i + e, tsrc, rsrc);
+  };
+  // hook(i) runs after the reads issued with batch i (a place for a direct load:
+  // issued between MFMAs, a wave's loads never queue up behind a burst)
+  const auto mfma_phase = [&](auto kind, const char* tsrc, const char* rsrc, auto hook)
+                              __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    const auto do_mfma = [&](int i, bf16x8 a) __attribute__((always_inline)) {
+      if (i < 16) {
+        const int kb = i >> 2, db = i & 3;
+        gacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ob[kb], gacc[db], 0, 0, 0);
+      } else {
+        const int j = i - 16, kk = j >> 1, mb = j & 1;
+        const f32x16 zero = {};
+        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kvf[kk], kk ? sc[mb] : zero, 0, 0, 0);
+      }
+    };
+    constexpr int first_i = K == 0 ? 16 : 0, last_i = K == 1 ? 16 : 32;
+#pragma unroll
+    for (int b = first_i; b < last_i; b += 4) {
+      const int cur = ((b - first_i) >> 2) % 3;
+      do_mfma(b, op[cur][0]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (b + 8 < last_i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[(cur + 2) % 3][e] = load_op(b + 8 + e, tsrc, rsrc);
+        if (b + 8 < 16)
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      hook((b - first_i) >> 2);
+#pragma unroll
+      for (int e = 1; e < 4; ++e) do_mfma(b + e, op[cur][e]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
+  };
+
+  // The per-query words a VALU phase needs (LSE2 for P, Delta for dS) are read
+  // into registers at the end of the wave's MFMA phase, and the mask is applied
+  // to S there: with the other wave's operand reads in the LDS queue, every
+  // LDS read left in a VALU phase costs its full latency.
+  f32x4 qw[8];  // LSE2 (P wave) or Delta (D wave) of queries 32mb + 8g + 4hi .. +3
+  const auto read_words = [&](const char* stage, int off) __attribute__((always_inline)) {
+    const float* w = (const float*)(stage + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qw[i] = *(const f32x4*)(w + (i >> 2) * 32 + 8 * (i & 3) + 4 * hi);
+  };
+  const auto mask_scores = [&](const char* stage) __attribute__((always_inline)) {
+    const int32_t* qi = (const int32_t*)(stage + kSpIds);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int4 t4 = *(const int4*)(qi + mb * 32 + 8 * g + 4 * hi);  // -1 past the end
+        sc[mb][4 * g + 0] = (kvalid & (t4.x == kid)) ? sc[mb][4 * g + 0] : -INFINITY;
+        sc[mb][4 * g + 1] = (kvalid & (t4.y == kid)) ? sc[mb][4 * g + 1] : -INFINITY;
+        sc[mb][4 * g + 2] = (kvalid & (t4.z == kid)) ? sc[mb][4 * g + 2] : -INFINITY;
+        sc[mb][4 * g + 3] = (kvalid & (t4.w == kid)) ? sc[mb][4 * g + 3] : -INFINITY;
+      }
+  };
+  // P wave VALU phase: P = exp2(S s2 - LSE2) (0 on masked scores), packed to
+  // bf16 (queries 32mb + 8(j/4) + 4hi + j%4 of the lane's key), handed over
+  const auto p_phase = [&](auto mid) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (mb == 1) mid();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = qw[4 * mb + g];
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[mb][4 * g + e], s2, -l4[e]));
+        const int kb = 2 * mb + (g >> 1), w0 = (g & 1) * 2;
+        u32x4 wp = __builtin_bit_cast(u32x4, ob[kb]);
+        wp[w0] = pack_bf16x2(p[0], p[1]);
+        wp[w0 + 1] = pack_bf16x2(p[2], p[3]);
+        ob[kb] = __builtin_bit_cast(bf16x8, wp);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) *(bf16x8*)(xb + kb * 1024 + lane * 16) = ob[kb];
+  };
+  // D wave VALU phase: dS = P (dP - Delta) from the handed-over P (same lanes)
+  const auto ds_phase = [&](auto mid) __attribute__((always_inline)) {
+    u32x4 wps[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) wps[kb] = *(const u32x4*)(xb + kb * 1024 + lane * 16);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb == 2) mid();
+      const u32x4 wp = wps[kb];
+      const int mb = kb >> 1;
+      u32x4 wd;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int g = 2 * (kb & 1) + h2;
+        const f32x4 d4 = qw[4 * mb + g];
+        const int w0 = 2 * h2;
+        const float p0 = bf16_bits_to_f32(wp[w0] & 0xFFFFu), p1 = bf16_bits_to_f32(wp[w0] >> 16);
+        const float p2 = bf16_bits_to_f32(wp[w0 + 1] & 0xFFFFu), p3 = bf16_bits_to_f32(wp[w0 + 1] >> 16);
+        wd[w0] = pack_bf16x2(p0 * (sc[mb][4 * g] - d4[0]), p1 * (sc[mb][4 * g + 1] - d4[1]));
+        wd[w0 + 1] = pack_bf16x2(p2 * (sc[mb][4 * g + 2] - d4[2]), p3 * (sc[mb][4 * g + 3] - d4[3]));
+      }
+      ob[kb] = __builtin_bit_cast(bf16x8, wd);
+    }
+  };
+  const auto pin_ob = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::"v"(ob[0]), "v"(ob[1]), "v"(ob[2]), "v"(ob[3]));
+  };
+
+  const auto barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using First = std::integral_constant<int, 0>;
+  using Last = std::integral_constant<int, 1>;
+  using Mid = std::integral_constant<int, 2>;
+  // step s: cur = stage of s, prev = stage of s - 1, ld = stage of s + 2
+  // (sub-tile s + 2 is staged during step s; each wave waits for its loads of
+  // step s at the end of step s + 1: they finish in order)
+  const auto step_p = [&](int s, auto kind, const char* cur, const char* prev, char* ld)
+                          __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    const int q0 = q0_of(s + 2, qt_l);
+    constexpr int nbat = K == 2 ? 8 : 4;
+    // dV (dO^T of s - 1), S (Q of s); piece 0 of s + 2 issued between MFMAs
+    mfma_phase(kind, prev + kSpSub, cur, [&](int i) __attribute__((always_inline)) {
+      if (K != 1 && i == 1) load_one(0, 0, q0, ld);
+      if (K != 1 && i == nbat - 2) load_one(1, 0, q0, ld);
+    });
+    if (K != 1) {
+      read_words(cur, kSpLse);
+      if (partial_c) mask_scores(cur);
+    }
+    barrier();
+    if (K != 1) load_one(0, 1, q0, ld);
+    fetch_next(s);
+    if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
+    if (K != 1) p_phase([&]() __attribute__((always_inline)) { load_one(1, 1, q0, ld); });
+    pin_ob();
+    land_next();
+    rotate();
+    if (K == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): this step's loads may stay
+    barrier();
+  };
+  const auto step_d = [&](int s, auto kind, const char* cur, const char* prev, char* ld)
+                          __attribute__((always_inline)) {
+    constexpr int K = decltype(kind)::value;
+    const int q0 = q0_of(s + 2, qt_l);
+    constexpr int nbat = K == 2 ? 8 : 4;
+    if (K != 1) load_one(0, 0, q0, ld);
+    fetch_next(s);
+    if (K != 0)
+      ds_phase([&]() __attribute__((always_inline)) {
+        if (K != 1) load_one(1, 0, q0, ld);
+      });
+    else
+      load_one(1, 0, q0, ld);
+    if (K != 1) load_words(q0, ld);
+    prefetch(kind, prev, cur + kSpSub);
+    pin_ob();
+    land_next();
+    barrier();
+    // dK (Q^T of s - 1), dP (dO of s); piece 1 of s + 2 issued between MFMAs
+    mfma_phase(kind, prev, cur + kSpSub, [&](int i) __attribute__((always_inline)) {
+      if (K != 1 && i == 1) load_one(0, 1, q0, ld);
+      if (K != 1 && i == nbat - 2) load_one(1, 1, q0, ld);
+    });
+    if (K != 1) read_words(cur, kSpDelta);  // Delta of s, for dS in the next step
+    rotate();
+    if (K == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+    barrier();
+  };
+  // prologue: sub-tiles 0 and 1 into stages 0 and 1
+  if (n > 0) {
+    const int qa = qt_of(0), qb = qt_of(1);
+    const int q00 = q0_of(0, qa), q01 = q0_of(1, qb);
+    load_piece(0, q00, st0);
+    load_piece(1, q00, st0);
+    load_piece(0, q01, st1);
+    load_piece(1, q01, st1);
+    if (grp == 1) {
+      load_words(q00, st0);
+      load_words(q01, st1);
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (n > 0) {
+    // step s (r = s % 4): cur st[r], prev st[(r + 3) % 4], loads into st[(r + 2) % 4]
+    const int rl = (n - 1) & 3;
+    char* const slast = rl == 0 ? st0 : rl == 1 ? st1 : rl == 2 ? st2 : st3;
+    if (grp == 0) {
+      prefetch(First{}, st3, st0);
+      step_p(0, First{}, st0, st3, st2);
+      for (int s = 1; s < n; s += 4) {
+        step_p(s, Mid{}, st1, st0, st3);
+        if (s + 1 < n) step_p(s + 1, Mid{}, st2, st1, st0);
+        if (s + 2 < n) step_p(s + 2, Mid{}, st3, st2, st1);
+        if (s + 3 < n) step_p(s + 3, Mid{}, st0, st3, st2);
+      }
+      step_p(n, Last{}, st0, slast, st2);
+    } else {
+      step_d(0, First{}, st0, st3, st2);
+      for (int s = 1; s < n; s += 4) {
+        step_d(s, Mid{}, st1, st0, st3);
+        if (s + 1 < n) step_d(s + 1, Mid{}, st2, st1, st0);
+        if (s + 2 < n) step_d(s + 2, Mid{}, st3, st2, st1);
+        if (s + 3 < n) step_d(s + 3, Mid{}, st0, st3, st2);
+      }
+      step_d(n, Last{}, st0, slast, st2);
+    }
+  }
+  if (kin) {
+    uint16_t* gp = (grp == 0 ? dv : dk) + (size_t)krow * rs + hoff;
+    const float f = grp == 0 ? 1.f : scale;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 a;
+        a[0] = pack_bf16x2(gacc[db][4 * g] * f, gacc[db][4 * g + 1] * f);
+        a[1] = pack_bf16x2(gacc[db][4 * g + 2] * f, gacc[db][4 * g + 3] * f);
+        *(u32x2*)(gp + db * 32 + 8 * g + 4 * hi) = a;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ fp32
 constexpr int kF32Sub = 32;
 
@@ -934,7 +1327,13 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                          mask->block_kv, mask->tile_class, mask->q_ptr, mask->q_cols,            \
                          mask->q_order, mask->nkv_tiles, (float*)dq);                            \
   } else {                                                                                       \
-    if (bf)                                                                                      \
+    if (bf && D == 128)                                                                          \
+      hipLaunchKernelGGL(dkdv_bf16_split_kernel<128>, gk, dim3(512), 0, s, (const uint16_t*)q,   \
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
+                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
+                         mask->tile_class, mask->kv_ptr, mask->kv_rows, mask->kv_order,          \
+                         mask->nkv_tiles, (uint16_t*)dk, (uint16_t*)dv);                         \
+    else if (bf)                                                                                 \
       hipLaunchKernelGGL(dkdv_bf16_kernel<D>, gk, dim3(256), 0, s, (const uint16_t*)q,           \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
                          lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
