@@ -460,6 +460,25 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // A barrier that also sets the issue priority for the phase it opens: the wave
+  // in its MFMA phase gets the higher one (by default the older wave of a SIMD
+  // wins every arbitration, stretching the other wave's phases of both kinds).
+  const auto barrier_mfma = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(2);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const auto barrier_valu = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   int partial_n = 0;
   const auto fetch_next = [&](int s) __attribute__((always_inline)) {
     partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
@@ -487,7 +506,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                           const char* vcur, char* kload) __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
     mfma_phase(kind, kcur, kprev, vcur, partial_c);
-    barrier();
+    barrier_valu();
     if (K != 1) {
       const int k0n = k0_of(last_sub(s + 2));
       const auto rk = rows(k, k0n);
@@ -500,7 +519,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     land_next();
     partial_c = partial_n;
     wait_prev_a(kind);
-    barrier();
+    barrier_mfma();
   };
   const auto step_b = [&](int s, auto kind, const char* kcur, const char* kprev,
                           const char* vcur, char* vload) __attribute__((always_inline)) {
@@ -513,11 +532,11 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     fetch_next(s);
     if (K != 0) valu_phase();
     land_next();
-    barrier();
+    barrier_mfma();
     mfma_phase(kind, kcur, kprev, vcur, partial_c);
     partial_c = partial_n;
     wait_prev_b(kind);
-    barrier();
+    barrier_valu();
   };
   using First = std::integral_constant<int, 0>;
   using Last = std::integral_constant<int, 1>;
@@ -545,6 +564,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   wait_vmem();
   __syncthreads();
+  if (grp == 0) __builtin_amdgcn_s_setprio(2);  // group A opens with its MFMA phase
   if (n > 0) {
     // step s (r = s % 4): kcur kb[r], kprev kb[(r + 3) % 4], vcur vb[r],
     // loads into kb[(r + 2) % 4] / vb[(r + 2) % 4]
@@ -1019,6 +1039,25 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // A barrier that also sets the issue priority for the phase it opens: the wave
+  // in its MFMA phase gets the higher one (by default the older wave of a SIMD
+  // wins every arbitration, stretching the other wave's phases of both kinds).
+  const auto barrier_mfma = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(2);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const auto barrier_valu = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   using First = std::integral_constant<int, 0>;
   using Last = std::integral_constant<int, 1>;
   using Mid = std::integral_constant<int, 2>;
@@ -1039,7 +1078,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       read_words(cur, kSpLse);
       if (partial_c) mask_scores(cur);
     }
-    barrier();
+    barrier_valu();
     if (K != 1) load_one(0, 1, q0, ld);
     fetch_next(s);
     if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
@@ -1051,7 +1090,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else
       __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): this step's loads may stay
-    barrier();
+    barrier_mfma();
   };
   const auto step_d = [&](int s, auto kind, const char* cur, const char* prev, char* ld)
                           __attribute__((always_inline)) {
@@ -1070,7 +1109,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     prefetch(kind, prev, cur + kSpSub);
     pin_ob();
     land_next();
-    barrier();
+    barrier_mfma();
     // dK (Q^T of s - 1), dP (dO of s); piece 1 of s + 2 issued between MFMAs
     mfma_phase(kind, prev, cur + kSpSub, [&](int i) __attribute__((always_inline)) {
       if (K != 1 && i == 1) load_one(0, 1, q0, ld);
@@ -1082,7 +1121,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else
       __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
-    barrier();
+    barrier_valu();
   };
   // prologue: sub-tiles 0 and 1 into stages 0 and 1
   if (n > 0) {
@@ -1099,6 +1138,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   }
   wait_vmem();
   __syncthreads();
+  if (grp == 0) __builtin_amdgcn_s_setprio(2);  // the P wave opens with its MFMA phase
   if (n > 0) {
     // step s (r = s % 4): cur st[r], prev st[(r + 3) % 4], loads into st[(r + 2) % 4]
     const int rl = (n - 1) & 3;
