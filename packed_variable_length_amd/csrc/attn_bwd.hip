@@ -350,12 +350,18 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int blk = wq + 4 * j;
     dma_b128(r, lane_off + blk * group_bytes, lds_address(dst + blk * 1024));
   };
+  // (buffer form inside the keys; the tail sub-tile takes the per-lane form,
+  // which gives keys past the end the id -1)
   const auto load_ids = [&](int k0, char* kdst) __attribute__((always_inline)) {
     // the lane index recomputed here (mbcnt) rather than kept live across the loop
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     if ((ln >> 4) == wq) {
       const int i = k0 + ln;
-      dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kDqSub));
+      if (k0 + 64 <= nkv)
+        dma_b32_buf(raw_rsrc(kv_ids, (uint32_t)nkv * 4u), (uint32_t)i * 4u,
+                    lds_address(kdst + kDqSub));
+      else
+        dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kDqSub));
     }
   };
 
@@ -886,16 +892,24 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     load_one(1, j, q0, stage);
   };
   // D wave wq stages the ids (0), LSE2 (1) or Delta (2, and again 3) of 64 queries
-  // (so each D wave issues 5 loads per step, each P wave 4)
+  // (so each D wave issues 5 loads per step, each P wave 4): the buffer form
+  // inside the queries, the per-lane form for the tail sub-tile (ids -1 past
+  // the end)
   const auto load_words = [&](int q0, char* stage) __attribute__((always_inline)) {
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int i = q0 + ln;
-    const void* src;
-    if (wq == 0)
-      src = i < nq ? q_ids + i : &kNoId;
-    else
-      src = (wq == 1 ? lse2 : delta) + (size_t)h * nq + min(i, nq - 1);
-    dma_b32(src, lds_address(stage + (wq == 0 ? kSpIds : wq == 1 ? kSpLse : kSpDelta)));
+    const uint32_t dst = lds_address(stage + (wq == 0 ? kSpIds : wq == 1 ? kSpLse : kSpDelta));
+    if (q0 + 64 <= nq) {
+      const void* base = wq == 0 ? (const void*)q_ids : (const void*)((wq == 1 ? lse2 : delta) + (size_t)h * nq);
+      dma_b32_buf(raw_rsrc(base, (uint32_t)nq * 4u), (uint32_t)i * 4u, dst);
+    } else {
+      const void* src;
+      if (wq == 0)
+        src = i < nq ? q_ids + i : &kNoId;
+      else
+        src = (wq == 1 ? lse2 : delta) + (size_t)h * nq + min(i, nq - 1);
+      dma_b32(src, dst);
+    }
   };
 
   // MFMA phase: gacc += tsrc^T ob over the previous sub-tile (dV^T += dO^T P or

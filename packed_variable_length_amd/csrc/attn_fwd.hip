@@ -475,11 +475,16 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
   // Each wave of group A stages 16 of the sub-tile's 64 key ids (one load
   // with 16 active lanes), so every wave of a group issues the same number of
-  // loads per step.
+  // loads per step.  A sub-tile inside the keys takes the buffer form; the
+  // tail one the per-lane form, which gives keys past the end the id -1.
+  const u32x4_t ids_rsrc = raw_rsrc(kv_ids, (uint32_t)nkv * 4u);
   const auto load_ids = [&](int k0, char* kdst) __attribute__((always_inline)) {
     if ((lane >> 4) == wq) {
       const int i = k0 + lane;
-      dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kPrSub));
+      if (k0 + 64 <= nkv)
+        dma_b32_buf(ids_rsrc, (uint32_t)i * 4u, lds_address(kdst + kPrSub));
+      else
+        dma_b32(i < nkv ? kv_ids + i : &kNoId, lds_address(kdst + kPrSub));
     }
   };
   // wait until only this step's loads are outstanding (loads finish in order):

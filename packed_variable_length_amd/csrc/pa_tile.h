@@ -140,6 +140,15 @@ __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
                ::"v"(src), "s"(lds) : "memory");
 }
 
+// 4 bytes per lane from rsrc at byte offset voff to LDS (lane i at lds + 4 i).
+// Measured cheaper than dma_b32 in the paired kernels (the global form slowed
+// the other group's MFMA phase while in flight); reads past the descriptor's
+// range return 0, so callers keep dma_b32 where a tail needs another fill.
+__device__ __forceinline__ void dma_b32_buf(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
 // Class byte of tile pair `idx`, fetched as the aligned 32-bit word that holds
 // it: a uniform word address becomes a scalar (SMEM) load, which -- unlike a
 // vector byte load -- does not make the wave wait behind its outstanding
