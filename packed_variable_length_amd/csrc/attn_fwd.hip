@@ -459,6 +459,14 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Between a group's two phases only a scheduling fence: no LDS buffer is
+  // written in a step that another wave reads in it, and each group's own
+  // results stay in its registers, so one barrier per step suffices.
+  const auto fence = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   int partial_n = 0;
   const auto fetch_next = [&](int s) __attribute__((always_inline)) {
     partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
@@ -509,7 +517,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                           __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
     mfma_phase(kind, kcur, vprev, partial_c);
-    barrier();
+    fence();
     if (K != 1) {
       const int k0n = k0_of(last_sub(s + 2));
       const auto rk = rows(k, k0n);
@@ -536,7 +544,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     fetch_next(s);
     if (K != 0) softmax_phase();
     land_next();
-    barrier();
+    fence();
     mfma_phase(kind, kcur, vprev, partial_c);
     partial_c = partial_n;
     wait_prev_b(kind);
