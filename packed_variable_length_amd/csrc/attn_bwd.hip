@@ -823,6 +823,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   __shared__ __attribute__((aligned(1024))) char st2[kSpStage];
   __shared__ __attribute__((aligned(1024))) char st3[kSpStage];
   __shared__ __attribute__((aligned(1024))) char xch[4 * 4096];  // P, per key block
+  __shared__ int xdone[4];  // per wave pair: last step whose P the D wave has read
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int hi = lane >> 5, col = lane & 31;
@@ -1006,6 +1007,25 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         sc[mb][4 * g + 3] = (kvalid & (t4.w == kid)) ? sc[mb][4 * g + 3] : -INFINITY;
       }
   };
+  // The two waves of a pair meet once per step (the barrier that ends it), so
+  // the P wave must not overwrite the hand-over buffer with P of step s before
+  // its D wave has read P of step s - 1 there: the D wave posts each step it
+  // has read (release), the P wave waits for it (acquire) before writing --
+  // normally long done.  The wait is bounded, so it ends on every path.
+  int xstep = 0;  // the step whose P this wave writes / reads next
+  const auto wait_xch = [&]() __attribute__((always_inline)) {
+    if (xstep > 0) {
+      for (int tries = 0; tries < (1 << 20); ++tries) {
+        const int done = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&xdone[wq], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (done >= xstep) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  };
+  const auto post_xch = [&]() __attribute__((always_inline)) {
+    if (lane == 0) __hip_atomic_store(&xdone[wq], xstep, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   // P wave VALU phase: P = exp2(S s2 - LSE2) (0 on masked scores), packed to
   // bf16 (queries 32mb + 8(j/4) + 4hi + j%4 of the lane's key), handed over
   const auto p_phase = [&](auto mid) __attribute__((always_inline)) {
@@ -1025,6 +1045,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         ob[kb] = __builtin_bit_cast(bf16x8, wp);
       }
     }
+    wait_xch();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *(bf16x8*)(xb + kb * 1024 + lane * 16) = ob[kb];
   };
@@ -1056,6 +1077,11 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     asm volatile("" ::"v"(ob[0]), "v"(ob[1]), "v"(ob[2]), "v"(ob[3]));
   };
 
+  const auto fence = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   const auto barrier = []() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -1091,6 +1117,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   const auto step_p = [&](int s, auto kind, const char* cur, const char* prev, char* ld)
                           __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
+    xstep = s;
     const int q0 = q0_of(s + 2, qt_l);
     constexpr int nbat = K == 2 ? 8 : 4;
     // dV (dO^T of s - 1), S (Q of s); piece 0 of s + 2 issued between MFMAs
@@ -1102,7 +1129,8 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       read_words(cur, kSpLse);
       if (partial_c) mask_scores(cur);
     }
-    barrier_valu();
+    fence();
+    __builtin_amdgcn_s_setprio(0);
     if (K != 1) load_one(0, 1, q0, ld);
     fetch_next(s);
     if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
@@ -1119,21 +1147,25 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   const auto step_d = [&](int s, auto kind, const char* cur, const char* prev, char* ld)
                           __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
+    xstep = s;
     const int q0 = q0_of(s + 2, qt_l);
     constexpr int nbat = K == 2 ? 8 : 4;
     if (K != 1) load_one(0, 0, q0, ld);
     fetch_next(s);
-    if (K != 0)
+    if (K != 0) {
       ds_phase([&]() __attribute__((always_inline)) {
         if (K != 1) load_one(1, 0, q0, ld);
       });
-    else
+      post_xch();  // P of step s - 1 read: the P wave may write that of step s
+    } else {
       load_one(1, 0, q0, ld);
+    }
     if (K != 1) load_words(q0, ld);
     prefetch(kind, prev, cur + kSpSub);
     pin_ob();
     land_next();
-    barrier_mfma();
+    fence();
+    __builtin_amdgcn_s_setprio(2);
     // dK (Q^T of s - 1), dP (dO of s); piece 1 of s + 2 issued between MFMAs
     mfma_phase(kind, prev, cur + kSpSub, [&](int i) __attribute__((always_inline)) {
       if (K != 1 && i == 1) load_one(0, 1, q0, ld);
@@ -1147,6 +1179,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
     barrier_valu();
   };
+  if (tid < 4) xdone[tid] = 0;
   // prologue: sub-tiles 0 and 1 into stages 0 and 1
   if (n > 0) {
     const int qa = qt_of(0), qb = qt_of(1);
