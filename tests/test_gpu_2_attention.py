@@ -101,6 +101,40 @@ def test_bf16_interleaved_ids(pa, seed):
     _check(got, ref, qo, ko, "bf16")
 
 
+def _segments(lengths, gaps):
+    """Ids for consecutive segments 0, 1, ... of the given lengths, each preceded
+    by a run of `gaps[i]` padding tokens (-1)."""
+    parts = []
+    for i, (n, g) in enumerate(zip(lengths, gaps)):
+        parts += [np.full(g, -1, np.int32), np.full(n, i, np.int32)]
+    return np.concatenate(parts)
+
+
+# segment lengths around the 64-token sub-tile and 128-token tile sizes, with
+# padding runs that shift each segment against the tile grid
+BOUNDARY_LEN = [1, 63, 64, 65, 127, 128, 129, 191, 256, 257]
+BOUNDARY_GAP = [0, 5, 0, 64, 1, 0, 127, 3, 0, 33]
+
+
+@pytest.mark.parametrize("cross", [False, True])
+def test_bf16_boundary_lengths(pa, cross):
+    rng = np.random.default_rng(31 + cross)
+    qo = _segments(BOUNDARY_LEN, BOUNDARY_GAP)
+    # cross: the same segments with other lengths on the key side (one empty)
+    ko = (_segments([129, 64, 1, 0, 200, 63, 128, 65, 127, 300], [2, 0, 64, 7, 0, 1, 0, 0, 129, 5])
+          if cross else qo.copy())
+    H, d = 2, 128
+    s = wl.PackSpec("boundary", heads=H, head_dim=d, dtype="bf16", seed=31, value_std=0.5,
+                    segment_ids=qo)
+    q, _, _, do = wl.make_values(s)
+    nkv = len(ko)
+    kk = wl.round_to_bf16(rng.standard_normal((nkv, H, d)).astype(np.float32) * 0.5)
+    vv = wl.round_to_bf16(rng.standard_normal((nkv, H, d)).astype(np.float32) * 0.5)
+    got = _run_gpu(pa, q, kk, vv, do, ids_dev(qo), ids_dev(ko), "bf16", s.scale)
+    ref = oatt.forward_backward(q, kk, vv, do, qo, ko, s.scale)
+    _check(got, ref, qo, ko, "bf16")
+
+
 def test_bf16_all_padding_pack(pa):
     s = _spec([0, 0], 4, 32, 32, 2, 128, "bf16", 3)
     q, k, v, do = wl.make_values(s)
