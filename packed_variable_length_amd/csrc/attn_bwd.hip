@@ -236,9 +236,10 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // phase apart: group A runs the MFMA phase of sub-tile s (dQ^T += K^T dS^T of
 // s - 1, then S^T = K Q^T and dP^T = V dO^T of s) and then the VALU phase of
 // s (P = exp2(S s2 - LSE2), dS = P (dP - Delta)); group B the VALU phase of
-// s - 1 and then the MFMA phase of s.  K(s) is read in two steps (S of s,
-// dQ of s), so K and V each get four LDS buffers; sub-tiles are staged two
-// steps ahead by the group in its VALU phase (A: K and ids, B: V).
+// s - 1 and then the MFMA phase of s; one workgroup barrier per step.  K(s) is
+// read in two steps (S of s, dQ of s), so K and V each get four LDS buffers;
+// sub-tiles are staged two steps ahead by the group in its VALU phase (A: K
+// and ids, B: V).
 constexpr int kDqSub = 64 * kRowBytes;  // one 64-key sub-tile (16 KB)
 
 template <int D>
@@ -455,20 +456,14 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       dsb[kb] = __builtin_bit_cast(bf16x8, w);
     }
     // the results exist here: keeps the compiler from sinking this phase past
-    // the barrier that ends it, into the MFMA phase that uses it
+    // its end, into the MFMA phase that uses it
     asm volatile("" ::"v"(dsb[0]), "v"(dsb[1]), "v"(dsb[2]), "v"(dsb[3]));
   };
 
-  const auto barrier = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // A barrier that also sets the issue priority for the phase it opens: the wave
-  // in its MFMA phase gets the higher one (by default the older wave of a SIMD
-  // wins every arbitration, stretching the other wave's phases of both kinds).
+  // The barrier that ends a step also sets the issue priority for the phase it
+  // opens (as does the fence at mid-step): the wave in its MFMA phase gets the
+  // higher one (by default the older wave of a SIMD wins every arbitration,
+  // stretching the other wave's phases of both kinds).
   const auto barrier_mfma = []() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -791,11 +786,13 @@ dkdv_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // half of the one-wave kernel's registers (room to keep its operand reads
 // ahead of its MFMAs), and the two alternate one phase apart per 64-query
 // sub-step s:
-//   phase X: P wave MFMAs (dV of s - 1, S of s); D wave VALU (dS of s - 1)
-//   phase Y: P wave VALU (P of s, into LDS);     D wave MFMAs (dK of s - 1, dP of s)
-// so each SIMD holds one MFMA wave and one VALU wave at a time.  Sub-tile s
-// (Q, dO, ids, LSE2, Delta) is read from phase X of s to phase Y of s + 1: four
-// LDS stages, staged two steps ahead by direct loads from inline assembly.  The
+//   first half:  P wave MFMAs (dV of s - 1, S of s); D wave VALU (dS of s - 1)
+//   second half: P wave VALU (P of s, into LDS);     D wave MFMAs (dK of s - 1, dP of s)
+// so each SIMD holds one MFMA wave and one VALU wave at a time.  Only the end
+// of a step is a workgroup barrier; the hand-over of P is guarded pairwise (see
+// wait_xch / post_xch).  Sub-tile s (Q, dO, ids, LSE2, Delta) is read from the
+// first half of step s to the second half of step s + 1: four LDS stages,
+// staged two steps ahead by direct loads from inline assembly.  The
 // 32 row groups of a sub-tile are spread over all eight waves, and each wave
 // issues its loads one at a time between MFMAs or VALU work: a burst of direct
 // loads at a phase start stalls the issuing waves for hundreds of cycles.  A
@@ -1082,16 +1079,10 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  const auto barrier = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // A barrier that also sets the issue priority for the phase it opens: the wave
-  // in its MFMA phase gets the higher one (by default the older wave of a SIMD
-  // wins every arbitration, stretching the other wave's phases of both kinds).
+  // The barrier that ends a step also sets the issue priority for the phase it
+  // opens (as does the fence at mid-step): the wave in its MFMA phase gets the
+  // higher one (by default the older wave of a SIMD wins every arbitration,
+  // stretching the other wave's phases of both kinds).
   const auto barrier_mfma = []() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");

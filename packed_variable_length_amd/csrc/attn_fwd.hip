@@ -220,7 +220,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // Group A (waves 0-3) owns the first tile, group B (waves 4-7) the second,
 // wave w query rows 32(w%4)..+31 of its group's tile, each over all keys.  Both
 // groups walk the same 64-key sub-tiles, one phase apart (A: MFMA phase then
-// softmax; B: softmax then MFMA phase), so each K/V sub-tile staged in LDS
+// softmax; B: softmax then MFMA phase; one workgroup barrier per step, at its
+// end), so each K/V sub-tile staged in LDS
 // serves 256 query rows: half the staging traffic per flop of one tile per
 // workgroup.  The sub-tiles cover each tile's key-tile range [first, last] of
 // its list -- one range when the two overlap or touch, else both ranges one
@@ -448,7 +449,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pb[kb] = __builtin_bit_cast(bf16x8, w);
     }
     // the results exist here: keeps the compiler from sinking the softmax
-    // past the barrier that ends the phase, into the MFMA phase that uses it
+    // past the end of the phase, into the MFMA phase that uses it
     asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(lsum));
   };
 
@@ -475,8 +476,8 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     asm volatile("" ::"s"(partial_n));
   };
   // Three buffers each for K and V: sub-tile s sits in kb[s % 3] / vb[s % 3].
-  // Step s stages K(s + 2) (group A, during its MFMA phase) and V(s + 1)
-  // (group B, during its MFMA phase); each wave waits for its previous step's
+  // Step s stages K(s + 2) (group A) and V(s + 1) (group B), each group at the
+  // start of its softmax phase; each wave waits for its previous step's
   // loads at the end of step s + 1, so a load has two steps to land.  Past the
   // last sub-tile the loads re-read sub-tile n - 1 into the free buffer, which
   // keeps the per-step load count (and so the partial waits) fixed.
