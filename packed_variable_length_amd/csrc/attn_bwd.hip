@@ -1122,9 +1122,9 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     }
     fence();
     __builtin_amdgcn_s_setprio(0);
+    if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
     if (K != 1) load_one(0, 1, q0, ld);
     fetch_next(s);
-    if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
     if (K != 1) p_phase([&]() __attribute__((always_inline)) { load_one(1, 1, q0, ld); });
     pin_ob();
     land_next();
