@@ -116,14 +116,14 @@ BOUNDARY_LEN = [1, 63, 64, 65, 127, 128, 129, 191, 256, 257]
 BOUNDARY_GAP = [0, 5, 0, 64, 1, 0, 127, 3, 0, 33]
 
 
-@pytest.mark.parametrize("cross", [False, True])
-def test_bf16_boundary_lengths(pa, cross):
-    rng = np.random.default_rng(31 + cross)
+@pytest.mark.parametrize("cross,d", [(False, 128), (True, 128), (False, 64), (True, 64)])
+def test_bf16_boundary_lengths(pa, cross, d):
+    rng = np.random.default_rng(31 + cross + d)
     qo = _segments(BOUNDARY_LEN, BOUNDARY_GAP)
     # cross: the same segments with other lengths on the key side (one empty)
     ko = (_segments([129, 64, 1, 0, 200, 63, 128, 65, 127, 300], [2, 0, 64, 7, 0, 1, 0, 0, 129, 5])
           if cross else qo.copy())
-    H, d = 2, 128
+    H = 3 if d == 64 else 2
     s = wl.PackSpec("boundary", heads=H, head_dim=d, dtype="bf16", seed=31, value_std=0.5,
                     segment_ids=qo)
     q, _, _, do = wl.make_values(s)
