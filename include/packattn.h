@@ -230,6 +230,21 @@ int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                              const pa_block_mask* mask, void* dk, void* dv, void* stream);
 
 /*
+ * pa_test_set_handover_spin_limit -- test hook, not for production callers.
+ * In the bf16 dK/dV kernel for 128-wide heads, the two waves that share a SIMD
+ * hand the probabilities P over through LDS, and the writer waits (bounded) for
+ * the reader's release of the previous P.  A wait that runs out makes that
+ * wave write NaN into its dv rows instead of values, so a broken hand-over
+ * shows in the output.  This sets the bound, in polls of about 64 cycles, for
+ * launches made after the call in this process (host state, not thread-safe);
+ * a negative limit restores the default (2^20).  Returns the previous bound.
+ * With a limit of 0 every wait after a tile's first step runs out at once
+ * (no poll is made), which lets a test see the NaN path without any kernel
+ * waiting long.
+ */
+int32_t pa_test_set_handover_spin_limit(int32_t limit);
+
+/*
  * Frame-valid masked squared-error loss ("LingBot-VA packing" report, section
  * 2.1, compute_loss: on a padded pack the latent and action losses are averaged
  * over valid frames only).  A token is valid iff its seq id is >= 0:

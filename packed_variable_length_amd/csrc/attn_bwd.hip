@@ -812,7 +812,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
                        const uint8_t* __restrict__ tile_class,
                        const int32_t* __restrict__ kv_ptr, const int32_t* __restrict__ kv_rows,
                        const int32_t* __restrict__ kv_order, int32_t nkt,
-                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int32_t spin_limit) {
   static_assert(D == 128, "the split dK/dV kernel is laid out for 128-wide heads");
   constexpr int kDB = D / 32, kKK = D / 16;
   __shared__ __attribute__((aligned(1024))) char st0[kSpStage];
@@ -1008,16 +1008,21 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   // the P wave must not overwrite the hand-over buffer with P of step s before
   // its D wave has read P of step s - 1 there: the D wave posts each step it
   // has read (release), the P wave waits for it (acquire) before writing --
-  // normally long done.  The wait is bounded, so it ends on every path.
+  // normally long done.  The wait is bounded (spin_limit polls), so it ends on
+  // every path; a wait that runs out marks the wave, which then writes NaN
+  // instead of its dV rows, so a broken hand-over cannot pass unnoticed.
   int xstep = 0;  // the step whose P this wave writes / reads next
+  bool xfail = false;
   const auto wait_xch = [&]() __attribute__((always_inline)) {
     if (xstep > 0) {
-      for (int tries = 0; tries < (1 << 20); ++tries) {
+      int tries = 0;
+      for (; tries < spin_limit; ++tries) {
         const int done = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(&xdone[wq], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (done >= xstep) break;
         __builtin_amdgcn_s_sleep(1);
       }
+      xfail |= tries >= spin_limit;
     }
   };
   const auto post_xch = [&]() __attribute__((always_inline)) {
@@ -1222,6 +1227,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         u32x2 a;
         a[0] = pack_bf16x2(gacc[db][4 * g] * f, gacc[db][4 * g + 1] * f);
         a[1] = pack_bf16x2(gacc[db][4 * g + 2] * f, gacc[db][4 * g + 3] * f);
+        if (xfail) a[0] = a[1] = 0x7FC07FC0u;  // bf16 quiet NaN pair
         *(u32x2*)(gp + db * 32 + 8 * g + 4 * hi) = a;
       }
   }
@@ -1378,6 +1384,11 @@ void launch_preprocess(const void* o, const void* dout, const float* lse, int32_
                      (const T*)o, (const T*)dout, lse, nq, H, delta, lse2);
 }
 
+// Bound of the dK/dV kernel's hand-over wait, in polls of about 64 cycles each
+// (2^20: tens of milliseconds, against a normal wait of none).  Tests lower it
+// through pa_test_set_handover_spin_limit.
+int32_t g_xch_spin_limit = 1 << 20;
+
 // Launches one stage of the backward: 0 = preprocess, 1 = dQ, 2 = dK/dV.
 // `ws` holds Delta [H][nq] followed by LSE*log2(e) [H][nq].
 int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
@@ -1420,7 +1431,7 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
                          lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
                          mask->tile_class, mask->kv_ptr, mask->kv_rows, mask->kv_order,          \
-                         mask->nkv_tiles, (uint16_t*)dk, (uint16_t*)dv);                         \
+                         mask->nkv_tiles, (uint16_t*)dk, (uint16_t*)dv, g_xch_spin_limit);       \
     else if (bf)                                                                                 \
       hipLaunchKernelGGL(dkdv_bf16_kernel<D>, gk, dim3(256), 0, s, (const uint16_t*)q,           \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
@@ -1541,4 +1552,10 @@ extern "C" int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32
     if (st != PA_OK) return st;
   }
   return PA_OK;
+}
+
+extern "C" int32_t pa_test_set_handover_spin_limit(int32_t limit) {
+  const int32_t prev = g_xch_spin_limit;
+  g_xch_spin_limit = limit >= 0 ? limit : (1 << 20);
+  return prev;
 }

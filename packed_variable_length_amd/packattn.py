@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "masked_mse_fwd": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
         "masked_mse_fwd_bwd": (i32, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
+        "pa_test_set_handover_spin_limit": (i32, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -104,6 +105,12 @@ _lib = _load()
 
 def pa_status_str(status: int) -> str:
     return _lib.pa_status_str(int(status)).decode()
+
+
+def pa_test_set_handover_spin_limit(limit: int) -> int:
+    """Test hook: bound of the dK/dV kernel's P hand-over wait for later launches
+    (a negative limit restores the default); returns the previous bound."""
+    return int(_lib.pa_test_set_handover_spin_limit(int(limit)))
 
 
 def _check(status: int, where: str) -> None:

@@ -208,6 +208,40 @@ def test_backward_deterministic_and_mask_hazard(pa):
     _check(got, ref, qo, ko, "bf16")
 
 
+def test_handover_wait_that_runs_out_poisons_dv(pa):
+    """The dK/dV kernel (bf16, 128-wide heads) hands P from one wave to the
+    other through LDS behind a bounded wait.  Forced from the host to run out
+    (a bound of zero polls), the waiting waves write NaN into their dv rows
+    instead of values -- every key tile with work has such a wait -- and the
+    kernel still ends normally; back at the default bound the results match
+    the oracle again."""
+    s = _spec([5, 9, 3], 9, 32, 32, 2, 128, "bf16", 4)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    Q, K, V, DO = (to_dev(a, "bf16") for a in (q, k, v, do))
+    mask = pa.build_block_mask(qg, kg)
+    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask)
+    ntiles = (s.nkv + 127) // 128
+    tile_has_work = np.array([(ko[128 * t:128 * (t + 1)] >= 0).any() for t in range(ntiles)])
+    rows_with_work = np.repeat(tile_has_work, 128)[: s.nkv]
+    assert tile_has_work.any() and not tile_has_work.all()
+    default = pa.pa_test_set_handover_spin_limit(0)
+    try:
+        assert default == 1 << 20
+        _, _, dv = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask)
+        torch.cuda.synchronize()
+        dv = host64(dv)
+    finally:
+        assert pa.pa_test_set_handover_spin_limit(-1) == 0
+    assert np.isnan(dv[rows_with_work]).all()
+    assert (dv[~rows_with_work] == 0).all()
+    g = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask)
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(g[0]),
+               dk=host64(g[1]), dv=host64(g[2]))
+    _check(got, ref, qo, ko, "bf16")
+
+
 # ------------------------------------------------------------- full-size workloads
 def _full_size(pa, s, heads):
     print(f"[full-size] {s.name} nq={s.nq} nkv={s.nkv} heads checked {heads}", flush=True)
