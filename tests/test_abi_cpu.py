@@ -120,6 +120,35 @@ def test_attention_argument_errors(lib):
                                FAKE, FAKE, None) == PA_ERR_NULL
 
 
+def test_backward_stage_argument_errors(lib):
+    # the three stage entry points check their arguments like attn_packed_bwd,
+    # before anything is launched
+    ws = lib.attn_packed_bwd_workspace_bytes(1, 500, 500, 2, 128)
+    pre = lib.attn_packed_bwd_preprocess
+    assert pre(1, 500, 2, 128, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == PA_ERR_WORKSPACE
+    assert pre(1, 500, 2, 128, None, FAKE, FAKE, FAKE, ws, None) == PA_ERR_NULL
+    assert pre(1, 500, 2, 128, FAKE, FAKE, None, FAKE, ws, None) == PA_ERR_NULL
+    assert pre(1, 500, 2, 96, FAKE, FAKE, FAKE, FAKE, ws, None) == PA_ERR_HEADDIM
+    assert pre(7, 500, 2, 128, FAKE, FAKE, FAKE, FAKE, ws, None) == PA_ERR_DTYPE
+    assert pre(1, 0, 2, 128, FAKE, FAKE, FAKE, FAKE, ws, None) == PA_ERR_SHAPE
+    assert pre(1, 500, 2, 128, FAKE, FAKE, FAKE, ctypes.c_void_p(0x200080), ws,
+               None) == PA_ERR_ALIGN
+    good, bad = _fake_mask(500, 500), _fake_mask(500, 600)
+
+    def dq(mask, wsb, out=FAKE):
+        return lib.attn_packed_bwd_dq(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, wsb, FAKE, FAKE, ctypes.byref(mask), out, None)
+
+    def dkdv(mask, wsb, out=FAKE):
+        return lib.attn_packed_bwd_dkdv(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, wsb, FAKE, FAKE, ctypes.byref(mask), FAKE, out,
+                                        None)
+    for stage in (dq, dkdv):
+        assert stage(bad, ws) == PA_ERR_MASK_MISMATCH
+        assert stage(good, ws - 1) == PA_ERR_WORKSPACE
+        assert stage(good, ws, out=None) == PA_ERR_NULL
+
+
 def test_mask_shape_hazard_is_rejected(lib):
     # a mask built for another shape (the packing report's forward/backward
     # ordering hazard) is refused before anything runs
