@@ -153,6 +153,14 @@ int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const int32_t* kv_
  * (natural log, fp32).  Rows with no allowed key: O = 0, LSE = -inf.
  * Work per query tile runs only over its non-empty key tiles; the elementwise
  * mask is applied only on partial tiles.
+ * Passages: the forward template of the masked attention kernel that runs on
+ * the packed pack ("LingBot-VA attention profiling" report, kernel profile:
+ * FlexAttention forward); the same-id predicate ("LingBot-VA attention
+ * profiling" report, next steps; "Furniture packing, variable length" report,
+ * implementation part: -1 removed as query and as key); fully masked padding
+ * rows must come out without NaN ("LingBot-VA packing" report, section 3.1
+ * table); packed output equals each episode run alone (same report, section
+ * 2.2).
  *
  *   dtype      PA_BF16 (bf16 in/out, fp32 accumulation; head_dim 64 or 128;
  *              the mask must use 128 x 128 tiles) or PA_F32 (fp32 throughout;
@@ -173,7 +181,10 @@ int32_t attn_packed_fwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, i
                         const pa_block_mask* mask, void* o, float* lse, void* stream);
 
 /* Workspace bytes attn_packed_bwd needs (fp32 Delta = rowsum(dO*O) and the LSE in
- * log2 units, each [heads][nq]), or 0 for invalid sizes. */
+ * log2 units, each [heads][nq]), or 0 for invalid sizes.  These row terms are
+ * the standard softmax-gradient quantities of the backward template the pages
+ * run ("LingBot-VA attention profiling" report, kernel profile: FlexAttention
+ * backward). */
 size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                                        int32_t head_dim);
 
@@ -183,7 +194,15 @@ size_t attn_packed_bwd_workspace_bytes(int32_t dtype, int32_t nq, int32_t nkv, i
  *   Delta = rowsum(dout * o), dS = P * (dout V^T - Delta),
  *   dq = scale dS K, dk = scale dS^T Q, dv = P^T dout.
  * Rows of dq with no allowed key, and rows of dk/dv that no query selects, are
- * exact zeros.  Arguments as for attn_packed_fwd, plus
+ * exact zeros.
+ * Passages: the backward template of the masked attention kernel
+ * ("LingBot-VA attention profiling" report, kernel profile: FlexAttention
+ * backward); gradients must stay finite on a pack with padding frames and the
+ * packed gradients match per-episode runs ("LingBot-VA packing" report,
+ * section 3.1 table and section 2.2); the mask shared by forward and backward
+ * must match the call (same report, section 2.2: a forward of another shape in
+ * between broke the backward), hence PA_ERR_MASK_MISMATCH.
+ * Arguments as for attn_packed_fwd, plus
  *   o, lse      the forward's outputs
  *   dout        device [nq][heads][head_dim] of `dtype`
  *   dq, dk, dv  device outputs of `dtype`, written (all rows)

@@ -1050,6 +1050,10 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     wait_xch();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *(bf16x8*)(xb + kb * 1024 + lane * 16) = ob[kb];
+    // The D wave reads this P right after the barrier that ends the step, and
+    // s_barrier does not wait for a wave's outstanding LDS writes: wait for
+    // them here (LDS counter only, so the step's direct loads stay in flight).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   // D wave VALU phase: dS = P (dP - Delta) from the handed-over P (same lanes)
   const auto ds_phase = [&](auto mid) __attribute__((always_inline)) {

@@ -122,7 +122,9 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None) -> None:
+    """Check placement, layout, dtype and (when given) the exact shape: the C ABI
+    receives bare pointers, so a buffer of the wrong size must be refused here."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
     if not t.is_contiguous():
@@ -131,6 +133,8 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 # --------------------------------------------------------------------- seq ids
@@ -208,6 +212,9 @@ def build_block_mask(q_seq_id: torch.Tensor, kv_seq_id: torch.Tensor, block_q: i
         raise PackAttnError(-2, "build_block_mask_bytes")
     if storage is None:
         storage = torch.empty(nbytes, dtype=torch.uint8, device=q_seq_id.device)
+    _need(storage, "storage", torch.uint8, q_seq_id.device)
+    if storage.dim() != 1:
+        raise ValueError("storage must be a flat uint8 tensor")
     desc = PaBlockMask()
     _check(_lib.build_block_mask(q_seq_id.data_ptr(), nq, kv_seq_id.data_ptr(), nkv,
                                  int(block_q), int(block_kv), storage.data_ptr(),
@@ -243,8 +250,8 @@ def attn_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_seq_id:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", q.dtype, q.device)
-    _need(lse_t, "lse", torch.float32, q.device)
+    _need(o, "out", q.dtype, q.device, q.shape)
+    _need(lse_t, "lse", torch.float32, q.device, (H, nq))
     _check(_lib.attn_packed_fwd(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
                                 k.data_ptr(), v.data_ptr(), q_seq_id.data_ptr(),
                                 kv_seq_id.data_ptr(), ctypes.byref(mask.desc), o.data_ptr(),
@@ -272,15 +279,21 @@ def attn_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     nq, nkv, H, d = _attn_shapes(q, k, v)
     if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (H, nq):
         raise ValueError("o / dout / lse shapes do not match q")
+    if q_seq_id.numel() != nq or kv_seq_id.numel() != nkv:
+        raise ValueError("seq id lengths do not match q / k")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
+    _need(dq, "dq", q.dtype, q.device, q.shape)
+    _need(dk, "dk", q.dtype, q.device, k.shape)
+    _need(dv, "dv", q.dtype, q.device, v.shape)
     nbytes = attn_packed_bwd_workspace_bytes(q.dtype, nq, nkv, H, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, q.device)
     _check(_lib.attn_packed_bwd(_DTYPES[q.dtype], nq, nkv, H, d, float(scale), q.data_ptr(),
                                 k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                                 lse.data_ptr(), q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
@@ -316,10 +329,12 @@ def _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale):
     nq, nkv, H, d = _attn_shapes(q, k, v)
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, name, q.dtype, q.device)
-    _need(lse, "lse", torch.float32, q.device)
+    _need(lse, "lse", torch.float32, q.device, (H, nq))
     _need(workspace, "workspace", torch.uint8, q.device)
-    _need(q_seq_id, "q_seq_id", torch.int32, q.device)
-    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device)
+    _need(q_seq_id, "q_seq_id", torch.int32, q.device, (nq,))
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device, (nkv,))
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return nq, nkv, H, d, float(scale)
@@ -329,6 +344,7 @@ def attn_packed_bwd_dq(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mask:
                        scale: Optional[float] = None, dq: Optional[torch.Tensor] = None):
     nq, nkv, H, d, scale = _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale)
     dq = torch.empty_like(q) if dq is None else dq
+    _need(dq, "dq", q.dtype, q.device, q.shape)
     _check(_lib.attn_packed_bwd_dq(_DTYPES[q.dtype], nq, nkv, H, d, scale, q.data_ptr(),
                                    k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), q_seq_id.data_ptr(),
@@ -343,6 +359,8 @@ def attn_packed_bwd_dkdv(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mas
     nq, nkv, H, d, scale = _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _need(dk, "dk", q.dtype, q.device, k.shape)
+    _need(dv, "dv", q.dtype, q.device, v.shape)
     _check(_lib.attn_packed_bwd_dkdv(_DTYPES[q.dtype], nq, nkv, H, d, scale, q.data_ptr(),
                                      k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(),
@@ -412,7 +430,7 @@ def masked_mse_fwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.Tenso
     """fp32 ``stats[4]`` = (loss, sum of squared errors, n_valid, 2/(n_valid*C))."""
     n, c, workspace = _loss_args(pred, target, seq_id, workspace)
     stats = torch.empty(4, dtype=torch.float32, device=pred.device) if stats is None else stats
-    _need(stats, "stats", torch.float32, pred.device)
+    _need(stats, "stats", torch.float32, pred.device, (4,))
     _check(_lib.masked_mse_fwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
                                seq_id.data_ptr(), stats.data_ptr(), workspace.data_ptr(),
                                workspace.numel(), _stream(pred)), "masked_mse_fwd")
@@ -425,9 +443,9 @@ def masked_mse_bwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.Tenso
     """Gradient of the loss w.r.t. ``pred`` (times ``upstream``), from forward ``stats``."""
     n, c, _ = _loss_args(pred, target, seq_id, torch.empty(1, dtype=torch.uint8,
                                                             device=pred.device))
-    _need(stats, "stats", torch.float32, pred.device)
+    _need(stats, "stats", torch.float32, pred.device, (4,))
     dpred = torch.empty_like(pred) if dpred is None else dpred
-    _need(dpred, "dpred", pred.dtype, pred.device)
+    _need(dpred, "dpred", pred.dtype, pred.device, pred.shape)
     _check(_lib.masked_mse_bwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
                                seq_id.data_ptr(), stats.data_ptr(), float(upstream),
                                dpred.data_ptr(), _stream(pred)), "masked_mse_bwd")
@@ -443,8 +461,8 @@ def masked_mse_fwd_bwd(pred: torch.Tensor, target: torch.Tensor, seq_id: torch.T
     n, c, workspace = _loss_args(pred, target, seq_id, workspace)
     stats = torch.empty(4, dtype=torch.float32, device=pred.device) if stats is None else stats
     dpred = torch.empty_like(pred) if dpred is None else dpred
-    _need(stats, "stats", torch.float32, pred.device)
-    _need(dpred, "dpred", pred.dtype, pred.device)
+    _need(stats, "stats", torch.float32, pred.device, (4,))
+    _need(dpred, "dpred", pred.dtype, pred.device, pred.shape)
     _check(_lib.masked_mse_fwd_bwd(_DTYPES[pred.dtype], n, c, pred.data_ptr(), target.data_ptr(),
                                    seq_id.data_ptr(), float(upstream), stats.data_ptr(),
                                    dpred.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -480,6 +498,9 @@ def adaln_fwd(x: torch.Tensor, seq_id: torch.Tensor, seg_offsets: torch.Tensor,
         rstd = torch.empty(n, dtype=torch.float32, device=x.device)
     else:
         y, mean, rstd = out
+    _need(y, "y", x.dtype, x.device, x.shape)
+    _need(mean, "mean", torch.float32, x.device, (n,))
+    _need(rstd, "rstd", torch.float32, x.device, (n,))
     _check(_lib.adaln_fwd(_DTYPES[x.dtype], n, d, n_seg, float(eps), x.data_ptr(),
                           seq_id.data_ptr(), seg_offsets.data_ptr(), shift.data_ptr(),
                           scale.data_ptr(), y.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
@@ -500,15 +521,18 @@ def adaln_bwd(x: torch.Tensor, dy: torch.Tensor, seq_id: torch.Tensor,
     _need(dy, "dy", x.dtype, x.device)
     if dy.shape != x.shape:
         raise ValueError("dy must match x")
-    _need(scale, "scale", torch.float32, x.device)
-    _need(mean, "mean", torch.float32, x.device)
-    _need(rstd, "rstd", torch.float32, x.device)
+    _need(scale, "scale", torch.float32, x.device, (n_seg, d))
+    _need(mean, "mean", torch.float32, x.device, (n,))
+    _need(rstd, "rstd", torch.float32, x.device, (n,))
     if out is None:
         dx = torch.empty_like(x)
         d_shift = torch.empty((n_seg, d), dtype=torch.float32, device=x.device)
         d_scale = torch.empty((n_seg, d), dtype=torch.float32, device=x.device)
     else:
         dx, d_shift, d_scale = out
+    _need(dx, "dx", x.dtype, x.device, x.shape)
+    _need(d_shift, "d_shift", torch.float32, x.device, (n_seg, d))
+    _need(d_scale, "d_scale", torch.float32, x.device, (n_seg, d))
     nbytes = adaln_bwd_workspace_bytes(n, d, n_seg)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)

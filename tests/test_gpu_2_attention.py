@@ -296,3 +296,52 @@ def test_full_bucketed_largest_self_and_cross(pa):
     _full_size(pa, wl.config(4), [0])
     cross = max(wl.bucketed_sweep(cross=True), key=lambda p: p.nq)
     _full_size(pa, cross, [17])
+
+
+def test_binding_refuses_wrong_output_buffers(pa):
+    """The C ABI takes bare pointers, so the binding must refuse an output or
+    workspace of the wrong shape, dtype or layout before anything is launched."""
+    s = _spec([5, 9, 3], 9, 6, 32, 2, 128, "bf16", 5)  # cross: nq != nkv
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    Q, K, V, DO = (to_dev(a, "bf16") for a in (q, k, v, do))
+    mask = pa.build_block_mask(qg, kg)
+    nq, nkv, H, d = Q.shape[0], K.shape[0], Q.shape[1], Q.shape[2]
+    dev = Q.device
+    bad_o = [torch.empty((nq - 1, H, d), dtype=torch.bfloat16, device=dev),
+             torch.empty((nq, H, d), dtype=torch.float32, device=dev),
+             torch.empty((nq, H, 2 * d), dtype=torch.bfloat16, device=dev)[..., :d]]
+    for o_bad in bad_o:
+        with pytest.raises(ValueError):
+            pa.attn_packed_fwd(Q, K, V, qg, kg, mask, out=o_bad)
+    with pytest.raises(ValueError):
+        pa.attn_packed_fwd(Q, K, V, qg, kg, mask,
+                           lse=torch.empty((H, nq - 1), dtype=torch.float32, device=dev))
+    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask)
+    good = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    for i, shape in ((0, (nq, H, d - 8)), (1, (nq, H, d)), (2, (nkv + 1, H, d))):
+        grads = list(good)
+        grads[i] = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        with pytest.raises(ValueError):
+            pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, grads=tuple(grads))
+    with pytest.raises(ValueError):  # seq ids of the wrong length
+        pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg[:-1].contiguous(), kg, mask)
+    with pytest.raises(ValueError):
+        pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask,
+                           workspace=torch.empty(16, dtype=torch.float32, device=dev))
+    ws = pa.attn_packed_bwd_preprocess(o, DO, lse)
+    with pytest.raises(ValueError):
+        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, ws, qg, kg, mask, dq=torch.empty_like(K))
+    with pytest.raises(ValueError):
+        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, qg, kg, mask, dk=torch.empty_like(Q))
+    with pytest.raises(ValueError):
+        pa.attn_packed_bwd_dq(Q, K, V, DO, lse[:, :-1].contiguous(), ws, qg, kg, mask)
+    with pytest.raises(ValueError):
+        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, qg, kg[:-1].contiguous(), mask)
+    # the checks refused everything above before a launch: the good call still matches
+    torch.cuda.synchronize()
+    dq, dk, dv = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, s.scale, grads=good)
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(dq),
+               dk=host64(dk), dv=host64(dv))
+    _check(got, ref, qo, ko, "bf16")
