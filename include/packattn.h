@@ -249,6 +249,33 @@ int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
                              const pa_block_mask* mask, void* dk, void* dv, void* stream);
 
 /*
+ * attn_packed_bwd_noalloc -- attn_packed_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and the same results, bit for bit,
+ * but the workspace (Delta and LSE2, 8 bytes per head and query) lives in a
+ * fixed array inside the library, one per device, held until the process ends.
+ * The entry point calls no hipMalloc, hipFree or allocating routine; on the
+ * first call made on a device it looks up that device's array address once.
+ *   Arguments, layouts and ownership as for attn_packed_bwd, without the
+ *   workspace.  Sizes: 8 * heads * nq (rounded up to 256) must not exceed
+ *   attn_packed_bwd_noalloc_max_bytes() (64 MiB: heads * nq <= 8,388,608),
+ *   else PA_ERR_WORKSPACE before any launch.
+ *   The array keeps the last call's contents; every value a call reads was
+ *   written by that call first, so no clearing is needed.  All calls on one
+ *   device share the array: calls that overlap in time on one device (other
+ *   streams, other host threads) race and must be serialised by the caller.
+ * Errors: as attn_packed_bwd; PA_ERR_HIP also if the array's address cannot be
+ * looked up.
+ */
+size_t attn_packed_bwd_noalloc_max_bytes(void);
+int32_t attn_packed_bwd_noalloc(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
+                                int32_t head_dim, float scale, const void* q, const void* k,
+                                const void* v, const void* o, const void* dout, const float* lse,
+                                const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                                const pa_block_mask* mask, void* dq, void* dk, void* dv,
+                                void* stream);
+
+/*
  * pa_test_set_handover_spin_limit -- test hook, not for production callers.
  * In the bf16 dK/dV kernel for 128-wide heads, the two waves that share a SIMD
  * hand the probabilities P over through LDS, and the writer waits (bounded) for

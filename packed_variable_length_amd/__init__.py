@@ -15,6 +15,8 @@ from .packattn import (  # noqa: F401
     attn_packed_bwd,
     attn_packed_bwd_dkdv,
     attn_packed_bwd_dq,
+    attn_packed_bwd_noalloc,
+    attn_packed_bwd_noalloc_max_bytes,
     attn_packed_bwd_preprocess,
     attn_packed_bwd_workspace_bytes,
     attn_packed_fwd,

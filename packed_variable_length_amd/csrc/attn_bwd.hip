@@ -28,8 +28,10 @@
 // (K^T, Q^T, dO^T) are read with ds_read_b64_tr_b16 from the same row-major
 // tiles (see pa_tile.h).
 #include <math.h>
-#include <type_traits>
 #include <limits.h>
+
+#include <mutex>
+#include <type_traits>
 
 #include "pa_common.h"
 #include "pa_tile.h"
@@ -1553,6 +1555,65 @@ extern "C" int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32
   for (int stage = 0; stage < 3; ++stage) {
     st = bwd_stage(stage, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse,
                    q_seq_id, kv_seq_id, mask, dq, dk, dv, (float*)workspace, s);
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+// ------------------------------------------------------- no-allocation backward
+// Fixed device-resident workspace for attn_packed_bwd_noalloc: callers that may
+// not allocate (graph capture, serving loops) still need the backward's row
+// terms (Delta and LSE2, 8 bytes per head and query).  Each device the library
+// runs on holds one copy of this array until the process ends.  Host code must
+// never pass `scratch` itself to a kernel (that is a host-side stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;  // H * nq <= 8,388,608
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call made with that device current), or nullptr on a HIP error.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t attn_packed_bwd_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int32_t attn_packed_bwd_noalloc(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
+                                           int32_t head_dim, float scale, const void* q,
+                                           const void* k, const void* v, const void* o,
+                                           const void* dout, const float* lse,
+                                           const int32_t* q_seq_id, const int32_t* kv_seq_id,
+                                           const pa_block_mask* mask, void* dq, void* dk,
+                                           void* dv, void* stream) {
+  int32_t st = pa::check_attn_args(dtype, nq, nkv, heads, head_dim, mask);
+  if (st != PA_OK) return st;
+  if (!lse || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if ((st = check_tensor(p))) return st;
+  const size_t need = workspace_bytes(dtype, nq, nkv, heads, head_dim);
+  if (need == 0 || need > kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+  float* ws = (float*)scratch_address();
+  if (!ws) return PA_ERR_HIP;
+  // Every entry of Delta and LSE2 that a later stage reads is written by the
+  // preprocess first, so nothing in the array needs clearing between calls.
+  const hipStream_t s = (hipStream_t)stream;
+  for (int stage = 0; stage < 3; ++stage) {
+    st = bwd_stage(stage, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse,
+                   q_seq_id, kv_seq_id, mask, dq, dk, dv, ws, s);
     if (st != PA_OK) return st;
   }
   return PA_OK;

@@ -92,6 +92,9 @@ def _load() -> ctypes.CDLL:
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
         "masked_mse_fwd_bwd": (i32, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
         "pa_test_set_handover_spin_limit": (i32, [i32]),
+        "attn_packed_bwd_noalloc_max_bytes": (sz, []),
+        "attn_packed_bwd_noalloc": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, pm, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -300,6 +303,43 @@ def attn_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
                                 ctypes.byref(mask.desc), dq.data_ptr(), dk.data_ptr(),
                                 dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                 _stream(q)), "attn_packed_bwd")
+    return dq, dk, dv
+
+
+def attn_packed_bwd_noalloc_max_bytes() -> int:
+    return int(_lib.attn_packed_bwd_noalloc_max_bytes())
+
+
+def attn_packed_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            dout: torch.Tensor, lse: torch.Tensor, q_seq_id: torch.Tensor,
+                            kv_seq_id: torch.Tensor, mask: BlockMask,
+                            scale: Optional[float] = None, grads=None
+                            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """attn_packed_bwd with the library's fixed per-device workspace (the C entry
+    point allocates nothing; pass ``grads`` to allocate nothing here either)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, q.dtype, q.device)
+    nq, nkv, H, d = _attn_shapes(q, k, v)
+    _need(lse, "lse", torch.float32, q.device, (H, nq))
+    _need(q_seq_id, "q_seq_id", torch.int32, q.device, (nq,))
+    _need(kv_seq_id, "kv_seq_id", torch.int32, q.device, (nkv,))
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o / dout shapes do not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+    _need(dq, "dq", q.dtype, q.device, q.shape)
+    _need(dk, "dk", q.dtype, q.device, k.shape)
+    _need(dv, "dv", q.dtype, q.device, v.shape)
+    _check(_lib.attn_packed_bwd_noalloc(_DTYPES[q.dtype], nq, nkv, H, d, float(scale),
+                                        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        dout.data_ptr(), lse.data_ptr(), q_seq_id.data_ptr(),
+                                        kv_seq_id.data_ptr(), ctypes.byref(mask.desc),
+                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(q)),
+           "attn_packed_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -169,6 +169,26 @@ def test_mask_shape_hazard_is_rejected(lib):
                                None) == PA_ERR_WORKSPACE
 
 
+def test_noalloc_backward_argument_errors(lib):
+    """The no-allocation backward checks its arguments like attn_packed_bwd and
+    refuses sizes past its fixed array (8 bytes per head and query, 64 MiB) on
+    the host: with no GPU here, getting past the checks would give PA_ERR_HIP."""
+    assert lib.attn_packed_bwd_noalloc_max_bytes() == 64 << 20
+
+    def call(nq, H, mask, dtype=1, d=128, out=FAKE):
+        return lib.attn_packed_bwd_noalloc(dtype, nq, 256, H, d, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, ctypes.byref(mask), out,
+                                           FAKE, FAKE, None)
+    H = 64
+    nq = (64 << 20) // (8 * H) + 128  # one 128-row tile past the limit
+    assert call(nq, H, _fake_mask(nq, 256)) == PA_ERR_WORKSPACE
+    assert call(nq - 128, H, _fake_mask(nq - 128, 256)) == PA_ERR_HIP  # fits: no GPU here
+    assert call(500, 2, _fake_mask(500, 600)) == PA_ERR_MASK_MISMATCH
+    assert call(500, 2, _fake_mask(500, 256), out=None) == PA_ERR_NULL
+    assert call(500, 2, _fake_mask(500, 256), d=96) == PA_ERR_HEADDIM
+    assert call(500, 2, _fake_mask(500, 256), dtype=3) == PA_ERR_DTYPE
+
+
 def test_tile_offset_identities():
     """The XOR forms of the LDS operand offsets equal the direct formulas
     (host re-implementation of the swizzle arithmetic in pa_tile.h)."""
