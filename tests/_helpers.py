@@ -74,3 +74,31 @@ def compare_lse(got, ref, heads=None, atol=1e-3):
     if (~ninf).any():
         d = float(np.abs(got[~ninf] - ref[~ninf]).max())
         assert d <= atol, f"LSE max abs diff {d:.3e} > {atol}"
+
+
+# ------------------------------------------------------------------ guard bands
+GUARD = 4096  # canary elements on each side of a guarded buffer (>= 8 KB, keeps alignment)
+_CANARY = {torch.bfloat16: (torch.int16, 0x7FA1), torch.float32: (torch.int32, 0x7FA00001),
+           torch.int32: (torch.int32, -0x5A5A5A5B), torch.uint8: (torch.uint8, 0xA5)}
+
+
+class Guarded:
+    """A device buffer that sits between two guard bands of a canary bit pattern
+    (a NaN for floating types, one no kernel writes).  The interior starts as the
+    same canary, so a row the kernel never writes is caught too (NaN, or the
+    pattern itself for integer storage).  ``check()`` asserts both bands are
+    untouched: a write past either end of the buffer fails it."""
+
+    def __init__(self, shape, dtype, device="cuda"):
+        n = 1
+        for s in shape:
+            n *= int(s)
+        itype, bits = _CANARY[dtype]
+        self.raw = torch.full((n + 2 * GUARD,), bits, dtype=itype, device=device)
+        self.tensor = self.raw.view(dtype)[GUARD:GUARD + n].view(*shape)
+        self.bits, self.n = bits, n
+
+    def check(self, name="buffer"):
+        lo, hi = self.raw[:GUARD], self.raw[GUARD + self.n:]
+        assert bool((lo == self.bits).all()), f"{name}: write before the start of the buffer"
+        assert bool((hi == self.bits).all()), f"{name}: write past the end of the buffer"

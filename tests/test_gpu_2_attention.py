@@ -1,8 +1,7 @@
 """GPU parity of packed masked attention (forward and backward) with the fp64 oracle.
 
-Small packs are compared element by element on every head; the full-size
-workloads are compared on a sample of heads (the oracle computes those heads
-completely) and checked on all heads for finiteness and exact-zero rows.
+Small packs are compared element by element on every head (the full-size
+workloads are in test_gpu_6_full_parity.py).
 Tolerances: see tests/_helpers.py.
 """
 import numpy as np
@@ -12,7 +11,8 @@ import torch
 import workloads as wl
 from oracle import attention as oatt
 from oracle import seqids as osid
-from tests._helpers import compare, compare_lse, host64, ids_dev, row_has_pair, to_dev
+from tests._helpers import (Guarded, compare, compare_lse, host64, ids_dev, row_has_pair,
+                            to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,11 +37,22 @@ def _ids_from_spec(pa, s):
 
 
 def _run_gpu(pa, q, k, v, do, qg, kg, dtype, scale, bq=128, bkv=128):
+    """Forward and backward with every output, the mask storage and the
+    workspace inside guard bands (interiors pre-filled with a NaN canary)."""
     Q, K, V, DO = (to_dev(a, dtype) for a in (q, k, v, do))
-    mask = pa.build_block_mask(qg, kg, bq, bkv)
-    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask, scale)
-    dq, dk, dv = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, scale)
+    nq, nkv, H, d = Q.shape[0], K.shape[0], Q.shape[1], Q.shape[2]
+    mstore = Guarded((pa.build_block_mask_bytes(nq, nkv, bq, bkv),), torch.uint8)
+    mask = pa.build_block_mask(qg, kg, bq, bkv, storage=mstore.tensor)
+    go, glse = Guarded(Q.shape, Q.dtype), Guarded((H, nq), torch.float32)
+    o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask, scale, out=go.tensor, lse=glse.tensor)
+    gq, gk, gv = Guarded(Q.shape, Q.dtype), Guarded(K.shape, K.dtype), Guarded(V.shape, V.dtype)
+    ws = Guarded((pa.attn_packed_bwd_workspace_bytes(Q.dtype, nq, nkv, H, d),), torch.uint8)
+    dq, dk, dv = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, scale,
+                                    workspace=ws.tensor, grads=(gq.tensor, gk.tensor, gv.tensor))
     torch.cuda.synchronize()
+    for name, g in (("mask storage", mstore), ("o", go), ("lse", glse), ("dq", gq), ("dk", gk),
+                    ("dv", gv), ("workspace", ws)):
+        g.check(name)
     return dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(dq),
                 dk=host64(dk), dv=host64(dv))
 
@@ -83,6 +94,32 @@ def test_bf16_small_packs_all_heads(pa, case):
     got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
     ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
     _check(got, ref, qo, ko, "bf16")
+
+
+# head counts that are multiples of 8 take the XCD head walk of the grid
+# mapping (XCD x runs heads x, x + 8, ...), the branch every production shape
+# (24 heads) takes: every head is compared, with NaN-filled outputs
+XCD_HEADS = [
+    ([5, 9, 0, 3, 7], 9, 32, 32, 8, 128),   # 1440 tokens, self
+    ([5, 9, 3], 9, 6, 32, 8, 128),          # cross-attention
+    ([5, 9, 0, 3, 7], 9, 32, 32, 16, 64),   # 64-wide heads
+    ([9, 2, 6], 9, 32, 32, 16, 128),        # 16 heads: two heads per XCD
+    ([4, 7], 8, 12, 32, 24, 64),            # 24 heads, cross, 64-wide
+]
+
+
+@pytest.mark.parametrize("case", range(len(XCD_HEADS)))
+def test_bf16_xcd_head_walk_all_heads(pa, case):
+    valid, fp, tq, tk, H, d = XCD_HEADS[case]
+    s = _spec(valid, fp, tq, tk, H, d, "bf16", 60 + case)
+    print(f"[xcd heads] H={H} d={d} nq={s.nq} nkv={s.nkv}", flush=True)
+    q, k, v, do = wl.make_values(s)
+    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
+    got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
+    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    _check(got, ref, qo, ko, "bf16")
+    for h in range(H):  # each head on its own: a swapped or missing head fails here
+        _check(got, ref, qo, ko, "bf16", heads=[h])
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -264,38 +301,6 @@ def test_handover_wait_that_runs_out_poisons_dv(pa):
     got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(g[0]),
                dk=host64(g[1]), dv=host64(g[2]))
     _check(got, ref, qo, ko, "bf16")
-
-
-# ------------------------------------------------------------- full-size workloads
-def _full_size(pa, s, heads):
-    print(f"[full-size] {s.name} nq={s.nq} nkv={s.nkv} heads checked {heads}", flush=True)
-    q, k, v, do = wl.make_values(s)
-    (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
-    got = _run_gpu(pa, q, k, v, do, qg, kg, "bf16", s.scale)
-    q_ok, k_ok = row_has_pair(qo, ko)
-    for name, ok in (("o", q_ok), ("dq", q_ok), ("dk", k_ok), ("dv", k_ok)):
-        assert np.isfinite(got[name]).all(), name
-        assert (got[name][~ok] == 0).all(), name
-    ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale, heads=heads)
-    return _check(got, ref, qo, ko, "bf16", heads)
-
-
-def test_full_var_4x288(pa):
-    _full_size(pa, wl.config(3), [0, 23])
-
-
-def test_full_equal_4x120(pa):
-    _full_size(pa, wl.config(2), [5])
-
-
-def test_full_long_mixed_64k(pa):
-    _full_size(pa, wl.config(5), [11])
-
-
-def test_full_bucketed_largest_self_and_cross(pa):
-    _full_size(pa, wl.config(4), [0])
-    cross = max(wl.bucketed_sweep(cross=True), key=lambda p: p.nq)
-    _full_size(pa, cross, [17])
 
 
 def test_binding_refuses_wrong_output_buffers(pa):

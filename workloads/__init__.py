@@ -14,6 +14,7 @@ from .packs import (  # noqa: F401
     bucketed_sweep,
     round_to_bf16,
     make_values,
+    make_sweep_values,
     make_loss_values,
     make_adaln_values,
     UNPADDED_BUDGET,

@@ -27,6 +27,7 @@ __all__ = [
     "bucketed_sweep",
     "round_to_bf16",
     "make_values",
+    "make_sweep_values",
     "make_loss_values",
     "make_adaln_values",
     "UNPADDED_BUDGET",
@@ -121,6 +122,23 @@ def make_values(spec: PackSpec):
         if spec.dtype == "bf16":
             a = round_to_bf16(a)
         out.append(a)
+    return tuple(out)
+
+
+def make_sweep_values(n_q: int, n_kv: int, heads: int, head_dim: int, seed=(4, 999),
+                      value_std: float = 0.5):
+    """One set of bf16-exact values (float32 arrays ``[n, heads, head_dim]``) large
+    enough for every batch of a sweep: a batch of nq query / nkv key tokens uses
+    the first nq rows of q and dO and the first nkv rows of k and v.  Draws as in
+    ``make_values`` (q, k, v, dO from ``np.random.default_rng(seed)``; q, k, v
+    scaled by ``value_std``; dO ~ N(0, 1)), so one draw serves all batches."""
+    rng = np.random.default_rng(list(seed))
+    out = []
+    for n, std in ((n_q, value_std), (n_kv, value_std), (n_kv, value_std), (n_q, 1.0)):
+        a = rng.standard_normal((int(n), int(heads), int(head_dim)), dtype=np.float32)
+        if std != 1.0:
+            a *= np.float32(std)
+        out.append(round_to_bf16(a))
     return tuple(out)
 
 
