@@ -11,7 +11,8 @@
     the batch maximum rounded up; the bucketing keeps padding waste on the
     160-episode stream under 10 % (the target the report sets);
   * the dual constraint (AdaptiveLoad summary, section 2A) by hand-worked
-    values, and every dual-constraint batch is within its bound and maximal;
+    values and a hand-cut pool; every dual-constraint batch is within its
+    bound, and no batch could take the next episode of its sorted pool;
   * the cost fit recovers (a, b, p) from exact synthetic timings.
 """
 import math
@@ -94,6 +95,46 @@ def test_dual_constraint_batches_are_within_bound_and_maximal():
         assert len(b) == 1 or len(b) <= osm.dual_constraint_batch(s, *dual[:3])
     sizes = [len(b) for b in batches]
     assert min(sizes) >= 1 and max(sizes) > 4      # short episodes get bigger batches
+
+
+def test_dual_constraint_cut_hand_worked_pool():
+    """One pool, cut by hand (AdaptiveLoad summary, section 2A, bound per batch;
+    32 tokens per frame, multiple of 8 frames, M_mem 68,000, M_comp 4e8, p 2):
+      * 100 frames -> S = 104*32 = 3,328, bound min(20, floor(36.1)) = 20;
+      * with a 200-frame episode S = 200*32 = 6,400, bound min(10, floor(9.77)) = 9:
+        seven 100s and two 200s make 9 <= 9, a third 200 would make 10 > 9 -> cut;
+      * the third 200 with the two 300s: S = 304*32 = 9,728, bound
+        min(6, floor(4.23)) = 4, so 3 <= 4 -> one batch to the end of the pool.
+    An off-by-one in the cut (closing a batch when it reaches the bound instead
+    of when it would exceed it) gives 8 + 4 instead of 9 + 3."""
+    frames = [100] * 7 + [200] * 3 + [300] * 2
+    dual = (68000.0, 4e8, 2.0, 32)
+    assert osm.dual_constraint_batch(3328, *dual[:3]) == 20
+    assert osm.dual_constraint_batch(6400, *dual[:3]) == 9
+    assert osm.dual_constraint_batch(9728, *dual[:3]) == 4
+    batches, fpad = osm.length_bucket_batches(frames, seed=5, epoch=0, pool_size=len(frames),
+                                              pad_multiple=8, dual=dual)
+    got = sorted(([frames[e] for e in b], f) for b, f in zip(batches, fpad))
+    assert got == [([100] * 7 + [200] * 2, 200), ([200, 300, 300], 304)]
+
+
+def test_dual_constraint_batches_cannot_grow():
+    """Maximality on the 160-episode stream, one pool: batches are consecutive
+    runs of the sorted pool, so ordered by (smallest, largest) frame count each
+    batch but the last would break its bound if it took the first episode of
+    the next one."""
+    fr = _frames()
+    dual = (68000.0, 4e8, 2.0, 32)
+    batches, _ = osm.length_bucket_batches(fr, seed=11, epoch=0, pool_size=len(fr),
+                                           pad_multiple=8, dual=dual)
+    runs = sorted(([fr[e] for e in b] for b in batches), key=lambda r: (min(r), max(r)))
+    assert [x for r in runs for x in sorted(r)] == sorted(fr)
+    for cur, nxt in zip(runs, runs[1:]):
+        grown = cur + [min(nxt)]
+        s = osm.round_up(max(grown), 8) * 32
+        assert len(grown) > osm.dual_constraint_batch(s, *dual[:3])
+        s_cur = osm.round_up(max(cur), 8) * 32
+        assert len(cur) == 1 or len(cur) <= osm.dual_constraint_batch(s_cur, *dual[:3])
 
 
 def test_cost_fit_recovers_exact_parameters():
