@@ -9,8 +9,15 @@ Inputs are synthetic (seeded, N(0,1)*0.5 bf16) and already resident in HBM.
 
 Prints ONE JSON line on stdout.  value = useful TFLOP/s = 14 * d * P * H /
 step time, where P counts only the allowed (same id, id >= 0) query-key pairs
-per head.  Per-stage times (HIP events on the stream the library launches on)
-go to stderr and into the JSON's "stages" object.
+per head (value_12dPH: the same time counted without the recompute).
+Per-stage times (HIP events on the stream the library launches on) go to
+stderr and into the JSON's "stages_ms" object.  After the timed steps the
+other workloads are measured the same way (extras.configs: the 4 x 120-frame
+pack, all 40 batches of the length-bucketed sweep, self and cross, and the
+64k mixed pack), the block-mask builder alone (extras.mask_builder: GB/s of
+its algorithmic bytes on the 4 x 288 and 64k packs and a 1,048,576-token case),
+then the next rows (masked loss, unpadded pack, planner, AdaLN) and the fp64
+CPU oracle on all heads of the pack (cpu_baseline).
 """
 import argparse
 import json
@@ -83,8 +90,9 @@ def cpu_baseline(spec, q, k, v, do, heads):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity size
         threads = len(os.sched_getaffinity(0))
-    ids = osid.seq_ids_from_valid_frames(spec.valid_frames, spec.frames_padded,
-                                         spec.q_tokens_per_frame)
+    ids = (spec.segment_ids if spec.segment_ids is not None else
+           osid.seq_ids_from_valid_frames(spec.valid_frames, spec.frames_padded,
+                                          spec.q_tokens_per_frame))
     t0 = time.perf_counter()
     oatt.forward_backward(q, k, v, do, ids, ids, spec.scale, heads=heads)
     dt = time.perf_counter() - t0
@@ -311,15 +319,228 @@ def run_extras(pa, spec, ids, extras):
         f"({r['speedup_vs_unfused']}x)")
 
 
+def _useful_pairs(q_ids, kv_ids):
+    """Allowed (query, key) pairs per head: for every id e >= 0, n_q(e) * n_kv(e)
+    (bench accounting of the useful work, from the ids the step built)."""
+    import numpy as np
+    qv, kv = q_ids[q_ids >= 0], kv_ids[kv_ids >= 0]
+    if qv.size == 0 or kv.size == 0:
+        return 0
+    m = int(max(qv.max(), kv.max())) + 1
+    return int((np.bincount(qv, minlength=m).astype(np.int64) *
+                np.bincount(kv, minlength=m).astype(np.int64)).sum())
+
+
+STAGES = ["seq_ids", "block_mask", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv"]
+
+
+class PackStep:
+    """One pass of the hot path over one pack: ids (from valid frames; given
+    directly for a pack of segment ids), block mask, forward, backward
+    preprocess, dQ, dK/dV.  Inputs are prefixes of caller buffers resident in HBM;
+    every output buffer is allocated here once."""
+
+    def __init__(self, pa, spec, Q, K, V, DO):
+        import torch
+        self.pa, self.spec = pa, spec
+        dev = Q.device
+        self.Q, self.K, self.V, self.DO = Q[:spec.nq], K[:spec.nkv], V[:spec.nkv], DO[:spec.nq]
+        nq, nkv, H, d = spec.nq, spec.nkv, spec.heads, spec.head_dim
+        if spec.segment_ids is not None:
+            self.vf = None
+            ids = torch.from_numpy(spec.segment_ids).to(dev)
+            self.qids, self.kids = ids, ids
+        else:
+            self.vf = torch.from_numpy(spec.valid_frames).to(dev)
+            self.qids = torch.empty(nq, dtype=torch.int32, device=dev)
+            self.kids = (self.qids if not spec.cross else
+                         torch.empty(nkv, dtype=torch.int32, device=dev))
+        self.O, self.dQ = torch.empty_like(self.Q), torch.empty_like(self.Q)
+        self.dK, self.dV = torch.empty_like(self.K), torch.empty_like(self.V)
+        self.lse = torch.empty((H, nq), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(pa.attn_packed_bwd_workspace_bytes(torch.bfloat16, nq, nkv, H, d),
+                              dtype=torch.uint8, device=dev)
+        self.mstore = torch.empty(pa.build_block_mask_bytes(nq, nkv, 128, 128),
+                                  dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.mask = None
+
+    def ids(self):
+        s = self.spec
+        if self.vf is not None:
+            self.pa.seq_ids_from_valid_frames(self.vf, s.frames_padded, s.q_tokens_per_frame,
+                                              out=self.qids)
+            if s.cross:
+                self.pa.seq_ids_from_valid_frames(self.vf, s.frames_padded,
+                                                  s.kv_tokens_per_frame, out=self.kids)
+
+    def build_mask(self):
+        self.mask = self.pa.build_block_mask(self.qids, self.kids, 128, 128, storage=self.mstore)
+        return self.mask
+
+    def __call__(self, ev=None):
+        pa, s = self.pa, self.spec
+
+        def mark(i):
+            if ev is not None:
+                ev[i].record(self.stream)
+        mark(0)
+        self.ids()
+        mark(1)
+        mask = self.build_mask()
+        mark(2)
+        pa.attn_packed_fwd(self.Q, self.K, self.V, self.qids, self.kids, mask, s.scale,
+                           out=self.O, lse=self.lse)
+        mark(3)
+        pa.attn_packed_bwd_preprocess(self.O, self.DO, self.lse, self.ws)
+        mark(4)
+        pa.attn_packed_bwd_dq(self.Q, self.K, self.V, self.DO, self.lse, self.ws, self.qids,
+                              self.kids, mask, s.scale, dq=self.dQ)
+        mark(5)
+        pa.attn_packed_bwd_dkdv(self.Q, self.K, self.V, self.DO, self.lse, self.ws, self.qids,
+                                self.kids, mask, s.scale, dk=self.dK, dv=self.dV)
+        mark(6)
+
+    def pairs(self):
+        import torch
+        torch.cuda.synchronize()
+        return _useful_pairs(self.qids.cpu().numpy(), self.kids.cpu().numpy())
+
+
+def time_steps(step, iters):
+    """(mean ms per step, mean ms per stage) from HIP events on the library's stream."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+             for j, n in enumerate(STAGES)}
+    total = float(np.mean([e[0].elapsed_time(e[6]) for e in evs]))
+    return total, stage
+
+
+def device_values(n_q, n_kv, heads, head_dim, seed, dev):
+    """Timing-only inputs drawn on the device: q, k, v ~ N(0,1)*0.5, dO ~ N(0,1), bf16
+    (the distribution of the seeded packs; the parity tests use the host draws)."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed)
+    mk = lambda n, sd: (sd * torch.randn((n, heads, head_dim), generator=g,  # noqa: E731
+                                         device=dev)).to(torch.bfloat16)
+    return mk(n_q, 0.5), mk(n_kv, 0.5), mk(n_kv, 0.5), mk(n_q, 1.0)
+
+
+def bench_pack_list(pa, specs, name, iters=5, warmup=1, seed=21):
+    """fwd+bwd of every pack in `specs` (one after the other, like the batches of
+    an epoch): summed time, summed useful flops, per-stage sums."""
+    import torch
+    dev = torch.device("cuda:0")
+    H, d = specs[0].heads, specs[0].head_dim
+    vals = device_values(max(s.nq for s in specs), max(s.nkv for s in specs), H, d, seed, dev)
+    total_ms, stages, pairs, tokens_q = 0.0, {n: 0.0 for n in STAGES}, 0, 0
+    for s in specs:
+        step = PackStep(pa, s, *vals)
+        for _ in range(warmup):
+            step()
+        ms, st = time_steps(step, iters)
+        total_ms += ms
+        for n in STAGES:
+            stages[n] += st[n]
+        pairs += step.pairs()
+        tokens_q += s.nq
+        del step
+    useful = 14.0 * d * pairs * H
+    tf = useful / (total_ms * 1e-3) / 1e12
+    return {"workload": name, "packs": len(specs), "query_tokens": tokens_q,
+            "valid_pairs_per_head": pairs, "useful_flops": useful, "ms": round(total_ms, 4),
+            "useful_TFLOPs": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "useful_TFLOPs_12dPH": round(tf * 12 / 14, 2),
+            "stages_ms": {n: round(v, 4) for n, v in stages.items()}}
+
+
+def mask_builder_bytes(nq, nkv, nnz, bq=128, bkv=128):
+    """Algorithmic HBM bytes of one block-mask build: the two id arrays read, the
+    class matrix (one byte per tile pair), both CSR lists (nnz entries each), their
+    row pointers and the two longest-first orders written."""
+    tq, tk = -(-nq // bq), -(-nkv // bkv)
+    return 4 * (nq + nkv) + tq * tk + 4 * 2 * nnz + 4 * (tq + tk + 2) + 4 * (tq + tk)
+
+
+def bench_mask_builder(pa, name, q_ids, kv_ids, iters=20):
+    """block_mask build alone: event-timed average and GB/s of its algorithmic bytes."""
+    import torch
+    nq, nkv = q_ids.numel(), kv_ids.numel()
+    store = torch.empty(pa.build_block_mask_bytes(nq, nkv, 128, 128), dtype=torch.uint8,
+                        device=q_ids.device)
+    ms = time_calls(lambda: pa.build_block_mask(q_ids, kv_ids, 128, 128, storage=store), iters)
+    mask = pa.build_block_mask(q_ids, kv_ids, 128, 128, storage=store)
+    nnz = int(mask.csr()[0][-1].item())
+    nbytes = mask_builder_bytes(nq, nkv, nnz)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "tokens": nq, "tiles": mask.nq_tiles * mask.nkv_tiles,
+            "nonempty_tiles": nnz, "avg_call_ms": round(ms, 5), "algorithmic_bytes": nbytes,
+            "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 5), "bound": "hbm (launch-latency at these sizes)"}
+
+
+def stress_ids(n=1 << 20, seg=4096):
+    """Ids of the mask-builder stress case: n tokens in consecutive segments of seg."""
+    import numpy as np
+    return (np.arange(n, dtype=np.int64) // seg).astype(np.int32)
+
+
+def run_configs(pa, configs, extras_out):
+    """The other workloads, each as whole fwd+bwd passes (summed over the packs
+    of the bucketed sweep), and the mask builder's GB/s."""
+    import torch
+
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    out = {}
+    for c in configs:
+        if c == "2":
+            out[c] = r = bench_pack_list(pa, [wl.config(2)], "equal-4x120")
+        elif c == "4self":
+            out[c] = r = bench_pack_list(pa, wl.bucketed_sweep(), "bucketed sweep, 40 batches")
+        elif c == "4cross":
+            out[c] = r = bench_pack_list(pa, wl.bucketed_sweep(cross=True),
+                                         "bucketed sweep, cross (6 action -> 32 video tok/frame)")
+        elif c == "5":
+            out[c] = r = bench_pack_list(pa, [wl.config(5)], "long-64k (ids given)")
+        else:
+            raise SystemExit(f"unknown config {c}")
+        log(f"[bench] config {c}: {r['ms']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful "
+            f"({100 * r['frac_of_bf16_peak']:.1f}% of bf16 peak)")
+    extras_out["configs"] = out
+    mb = {}
+    s3 = wl.config(3)
+    vf = torch.from_numpy(s3.valid_frames).to(dev)
+    ids3 = pa.seq_ids_from_valid_frames(vf, s3.frames_padded, s3.q_tokens_per_frame)
+    mb["3"] = bench_mask_builder(pa, "var-4x288", ids3, ids3)
+    ids5 = torch.from_numpy(wl.config(5).segment_ids).to(dev)
+    mb["5"] = bench_mask_builder(pa, "long-64k", ids5, ids5)
+    idss = torch.from_numpy(stress_ids()).to(dev)
+    mb["stress"] = bench_mask_builder(pa, "1,048,576 tokens in 4,096-token segments", idss, idss)
+    for k, r in mb.items():
+        log(f"[bench] mask builder {k}: {r['avg_call_ms'] * 1e3:.1f} us, "
+            f"{r['achieved_GBs']} GB/s of {r['algorithmic_bytes']} algorithmic bytes")
+    extras_out["mask_builder"] = mb
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload number (3 = the metric)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload of the timed steps (3 = the metric; 2 and 5 also run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=str, default="0,1,2,3,4,5,6,7",
-                    help="heads the oracle baseline computes (a bounded sample)")
+    ap.add_argument("--cpu-heads", type=str, default="all",
+                    help="heads the oracle baseline computes ('all' or a list like 0,23)")
+    ap.add_argument("--configs", type=str, default="2,4self,4cross,5",
+                    help="other workloads measured after the timed steps ('' for none)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the loss / unpadded-pack / planner / AdaLN measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -331,48 +552,19 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import packed_variable_length_amd as pa
     import workloads as wl
 
     spec = wl.config(args.config)
-    assert spec.dtype == "bf16" and spec.valid_frames is not None
+    assert spec.dtype == "bf16" and args.config in (2, 3, 5), "timed workload: 2, 3 or 5"
     log(f"[bench] workload {spec.name}: nq={spec.nq} heads={spec.heads} d={spec.head_dim}")
     q, k, v, do = wl.make_values(spec)
     dev = torch.device("cuda:0")
     T = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
-    Q, K, V, DO = T(q), T(k), T(v), T(do)
-    vf = torch.from_numpy(spec.valid_frames).to(dev)
+    step = PackStep(pa, spec, T(q), T(k), T(v), T(do))
     H, d, nq = spec.heads, spec.head_dim, spec.nq
-    ids = torch.empty(nq, dtype=torch.int32, device=dev)
-    O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
-    lse = torch.empty((H, nq), dtype=torch.float32, device=dev)
-    ws = torch.empty(pa.attn_packed_bwd_workspace_bytes(torch.bfloat16, nq, nq, H, d),
-                     dtype=torch.uint8, device=dev)
-    mstore = torch.empty(pa.build_block_mask_bytes(nq, nq, 128, 128), dtype=torch.uint8,
-                         device=dev)
-    stream = torch.cuda.current_stream(dev)
-    names = ["seq_ids", "block_mask", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv"]
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        pa.seq_ids_from_valid_frames(vf, spec.frames_padded, spec.q_tokens_per_frame, out=ids)
-        mark(1)
-        mask = pa.build_block_mask(ids, ids, 128, 128, storage=mstore)
-        mark(2)
-        pa.attn_packed_fwd(Q, K, V, ids, ids, mask, spec.scale, out=O, lse=lse)
-        mark(3)
-        pa.attn_packed_bwd_preprocess(O, DO, lse, ws)
-        mark(4)
-        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, ws, ids, ids, mask, spec.scale, dq=dQ)
-        mark(5)
-        pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, ids, ids, mask, spec.scale, dk=dK, dv=dV)
-        mark(6)
 
     for _ in range(args.warmup):
         step()
@@ -385,9 +577,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {n} bytes done")
         del src, dst
-    ids_h = ids.cpu().numpy()
-    valid = ids_h[ids_h >= 0]
-    pairs = int((np.bincount(valid).astype(np.int64) ** 2).sum())  # self-attention pack
+    pairs = step.pairs()
     useful = 14.0 * d * pairs * H
 
     # timed region: wall clock around exactly `steps` steps
@@ -398,18 +588,13 @@ def main():
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     # per-stage HIP events over a second pass of the same steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
-                for j, n in enumerate(names)}
-    for n in names:
+    _, stage_ms = time_steps(step, args.steps)
+    for n in STAGES:
         log(f"[bench] {n:10s} {stage_ms[n]:8.3f} ms")
     tflops = useful / wall / 1e12
     log(f"[bench] step {wall * 1e3:.3f} ms  useful {tflops:.1f} TFLOP/s "
-        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak; "
+        f"{tflops * 12 / 14:.1f} TFLOP/s counting 12*d*P*H, without the recompute)")
 
     kernels = {n: stage_ms[n] for n in FLOPS_PER_PAIR}
     dom = max(kernels, key=kernels.get)
@@ -423,31 +608,48 @@ def main():
                 "flops_per_launch": FLOPS_PER_PAIR[dom] * d * pairs * H,
                 "avg_launch_ms": round(kernels[dom], 4),
                 "source_sha256": source_sha256(dom)}
+    per_kernel = {n: {"ms": round(kernels[n], 4),
+                      "achieved_TFLOPs": round(FLOPS_PER_PAIR[n] * d * pairs * H
+                                               / (kernels[n] * 1e-3) / 1e12, 2)}
+                  for n in FLOPS_PER_PAIR}
+    del step
 
     extras = {}
+    cfgs = [c for c in args.configs.split(",") if c]
+    if cfgs:
+        run_configs(pa, cfgs, extras)
     if not args.no_extras:
-        run_extras(pa, spec, ids, extras)
+        s3 = wl.config(3)
+        ids3 = pa.seq_ids_from_valid_frames(torch.from_numpy(s3.valid_frames).to(dev),
+                                            s3.frames_padded, s3.q_tokens_per_frame)
+        run_extras(pa, s3, ids3, extras)
 
     cpu = None
     if not args.no_cpu_baseline:
-        heads = [int(x) for x in args.cpu_heads.split(",")]
+        heads = (list(range(spec.heads)) if args.cpu_heads == "all"
+                 else [int(x) for x in args.cpu_heads.split(",")])
         log(f"[bench] cpu baseline: oracle on heads {heads} ...")
         cpu = cpu_baseline(spec, q, k, v, do, heads)
         log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']} s")
 
+    if spec.segment_ids is not None:
+        wdesc = f"{spec.name}: {nq} tokens with given segment ids, {H} heads x {d}"
+    else:
+        wdesc = (f"{spec.name}: {spec.n_episodes} episodes of "
+                 f"{'/'.join(str(int(x)) for x in spec.valid_frames)} valid frames padded to "
+                 f"{spec.frames_padded}, 32 tokens/frame, {nq} tokens, {H} heads x {d}")
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 bf16; stands in for FurnitureBench episodes)",
-        "config": {"workload": f"{spec.name}: 4 episodes of "
-                               f"{'/'.join(str(int(x)) for x in spec.valid_frames)} valid frames "
-                               f"padded to {spec.frames_padded}, 32 tokens/frame, "
-                               f"{nq} tokens, {H} heads x {d}",
-                   "tokens": nq, "heads": H, "head_dim": d, "valid_pairs_per_head": pairs,
-                   "useful_flops": useful, "parallelism": "single GPU"},
+        "config": {"workload": wdesc, "tokens": nq, "heads": H, "head_dim": d,
+                   "valid_pairs_per_head": pairs, "useful_flops": useful,
+                   "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "stages_ms": {n: round(stage_ms[n], 4) for n in names},
+        "value_12dPH": round(tflops * 12 / 14, 2),
+        "stages_ms": {n: round(stage_ms[n], 4) for n in STAGES},
+        "kernels": per_kernel,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
