@@ -115,6 +115,16 @@ int32_t seq_ids_from_lengths(const int32_t* lengths, int32_t B, int32_t n_tokens
  * the tiles by decreasing list length (ties by ascending index); the attention
  * kernels use them to start the longest work first.
  *
+ * Pair lists: the query tiles at positions 2w and 2w + 1 of q_order form pair
+ * w (w < ceil(nq_tiles / 2); the last pair of an odd count has one tile).
+ * pair_ent[pair_off[w] .. pair_off[w] + pair_len[w]) lists, ascending, every
+ * key tile kt that either tile of the pair has an allowed pair with, as
+ * kt | class(first, kt) << 16 | class(second, kt) << 24 (class 0 for a tile
+ * outside that tile's list, and for a missing second tile).  pair_off[w] is
+ * the exclusive prefix sum over pairs of the two tiles' list lengths (room for
+ * the union; pair_off[last + 1] is the total).  The paired attention kernels
+ * walk these lists, so they visit exactly the key tiles with work.
+ *
  * All pointers in the descriptor point into the caller's `storage` buffer; the
  * descriptor itself is host memory, filled by build_block_mask.
  */
@@ -127,6 +137,9 @@ typedef struct pa_block_mask {
   int32_t* kv_rows;    /* device, capacity nq_tiles * nkv_tiles                 */
   int32_t* q_order;    /* device [nq_tiles]                                     */
   int32_t* kv_order;   /* device [nkv_tiles]                                    */
+  int32_t* pair_off;   /* device [ceil(nq_tiles / 2) + 1]                       */
+  int32_t* pair_len;   /* device [ceil(nq_tiles / 2)]                           */
+  int32_t* pair_ent;   /* device, capacity nq_tiles * nkv_tiles                 */
 } pa_block_mask;
 
 /* Bytes of device storage build_block_mask needs for these sizes, or 0 if the

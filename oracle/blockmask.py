@@ -78,3 +78,33 @@ def csr_lists(cls: np.ndarray):
 def class_totals(cls: np.ndarray):
     """(empty, partial, full) tile-pair counts."""
     return (int((cls == EMPTY).sum()), int((cls == PARTIAL).sum()), int((cls == FULL).sum()))
+
+
+def longest_first_order(cls: np.ndarray, axis: int = 0) -> np.ndarray:
+    """Tiles of one axis by decreasing number of non-empty partners, ties by
+    ascending index (``axis`` 0: query tiles, 1: key tiles)."""
+    lens = (cls != EMPTY).sum(axis=1 - axis)
+    return np.asarray(sorted(range(len(lens)), key=lambda t: (-int(lens[t]), t)), dtype=np.int32)
+
+
+def pair_lists(cls: np.ndarray, q_order: np.ndarray):
+    """The walk of each pair of query tiles (positions 2w and 2w + 1 of the
+    query order): every key tile that either tile has an allowed pair with,
+    ascending, encoded ``kt | class(first) << 16 | class(second) << 24`` (class
+    0 outside a tile's list and for a missing second tile).
+
+    Returns ``(room, lists)``: ``room`` is the exclusive prefix sum over pairs of
+    the two tiles' list lengths (``npairs + 1`` entries), ``lists`` one int32
+    array per pair."""
+    nqt, nkt = cls.shape
+    lens = (cls != EMPTY).sum(axis=1)
+    room, lists = [0], []
+    for w in range((nqt + 1) // 2):
+        a = int(q_order[2 * w])
+        b = int(q_order[2 * w + 1]) if 2 * w + 1 < nqt else -1
+        ra = cls[a].astype(np.int64)
+        rb = cls[b].astype(np.int64) if b >= 0 else np.zeros(nkt, np.int64)
+        cols = np.flatnonzero((ra != EMPTY) | (rb != EMPTY))  # ascending
+        lists.append((cols | (ra[cols] << 16) | (rb[cols] << 24)).astype(np.int32))
+        room.append(room[-1] + int(lens[a]) + (int(lens[b]) if b >= 0 else 0))
+    return np.asarray(room, dtype=np.int32), lists

@@ -234,7 +234,7 @@ dq_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // ------------------------------------------------------------------ bf16 dq, paired
 // 128-wide heads: a workgroup of 8 waves per pair of query tiles (positions 2w
 // and 2w + 1 of the longest-first order), one per wave group, like the
-// forward's paired kernel.  Both groups walk the same 64-key sub-tiles one
+// forward's paired kernel, walking the pair's list of the block mask.  Both groups walk the same 64-key sub-tiles one
 // phase apart: group A runs the MFMA phase of sub-tile s (dQ^T += K^T dS^T of
 // s - 1, then S^T = K Q^T and dP^T = V dO^T of s) and then the VALU phase of
 // s (P = exp2(S s2 - LSE2), dS = P (dP - Delta)); group B the VALU phase of
@@ -251,9 +251,9 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const float* __restrict__ delta, const float* __restrict__ lse2,
                     const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
                     int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
-                    const uint8_t* __restrict__ tile_class, const int32_t* __restrict__ q_ptr,
-                    const int32_t* __restrict__ q_cols, const int32_t* __restrict__ q_order,
-                    int32_t nkt, uint16_t* __restrict__ dq) {
+                    const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
+                    const int32_t* __restrict__ pair_len, const int32_t* __restrict__ pair_ent,
+                    uint16_t* __restrict__ dq) {
   static_assert(D == 128, "the paired dQ kernel is laid out for 128-wide heads");
   constexpr int kDB = D / 32, kKK = D / 16;
   __shared__ __attribute__((aligned(1024))) char kb0[kDqSub + 256];
@@ -273,34 +273,10 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   block_work(blockIdx.x, H, (nqt + 1) / 2, &work, &h);
   const int qpair[2] = {q_order[2 * work], 2 * work + 1 < nqt ? q_order[2 * work + 1] : -1};
   const int qmine = qpair[grp];  // -1: no tile (odd tile count), no rows, all masked
-  // the key walk: each tile's key-tile range [first, last] of its list; one
-  // segment when the two overlap or touch, else both one after the other
-  int first[2], last[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    first[g] = INT_MAX;
-    last[g] = -1;
-    if (qpair[g] >= 0 && q_ptr[qpair[g] + 1] > q_ptr[qpair[g]]) {
-      first[g] = q_cols[q_ptr[qpair[g]]];
-      last[g] = q_cols[q_ptr[qpair[g] + 1] - 1];
-    }
-  }
-  int lo0, len0, lo1 = 0, len1 = 0;
-  if (last[1] < 0 || (last[0] >= 0 && first[1] <= last[0] + 1 && first[0] <= last[1] + 1)) {
-    lo0 = min(first[0], first[1]);
-    len0 = max(last[0], last[1]) - lo0 + 1;
-  } else if (last[0] < 0) {
-    lo0 = first[1];
-    len0 = last[1] - first[1] + 1;
-  } else {
-    const int g0 = first[0] <= first[1] ? 0 : 1;
-    lo0 = first[g0];
-    len0 = last[g0] - first[g0] + 1;
-    lo1 = first[1 - g0];
-    len1 = last[1 - g0] - first[1 - g0] + 1;
-  }
-  if (len0 < 0) len0 = 0;
-  const int n = 2 * (len0 + len1);  // 64-key sub-steps
+  // the key walk: the pair's list from the block mask (key tiles one of the two
+  // query tiles has work with, ascending, both classes beside each tile)
+  const int32_t* const pent = pair_ent + pair_off[work];
+  const int n = 2 * pair_len[work];  // 64-key sub-steps
   const size_t rs = (size_t)H * D;
   const int hoff = h * D;
 
@@ -331,15 +307,22 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   f32x16 st[2], dpt[2];  // S^T, dP^T of the current sub-tile (keys 32mb + ...)
   bf16x8 dsb[4];         // dS^T of the previous one, as MFMA operands (16 keys each)
 
-  const auto tile_of = [&](int s) {
-    const int u = s >> 1;
-    return u < len0 ? lo0 + u : lo1 + (u - len0);
+  // walk entries as scalars, as in the paired forward: e1, e2 hold the entries
+  // of sub-steps s + 1 and s + 2 at step s; the entry of s + 3 is fetched in
+  // the step's VALU phase and landed at its end
+  const auto ent = [&](int s) { return pent[(s < n ? s : n - 1) >> 1]; };
+  const auto k0_of = [&](int e, int s) {
+    return (e & 0xFFFF) * 128 + 64 * ((s < n ? s : n - 1) & 1);
   };
-  const auto k0_of = [&](int s) { return tile_of(s) * 128 + 64 * (s & 1); };
-  const auto needs_mask = [&](int s) {
-    return qmine < 0 || tile_class_at(tile_class, (size_t)qmine * nkt + tile_of(s)) != 2;
-  };
-  bool partial_c = n > 0 && needs_mask(0);
+  const int csh = 16 + 8 * grp;
+  const auto needs_mask = [&](int e) { return ((e >> csh) & 0xFF) != 2; };
+  int e1 = 0, e2 = 0, e3 = 0;
+  bool partial_c = false;
+  if (n > 0) {
+    partial_c = needs_mask(ent(0));
+    e1 = ent(1);
+    e2 = ent(2);
+  }
 
   const uint32_t group_bytes = (uint32_t)(4 * rs * 2);
   const uint32_t lane_off =
@@ -492,12 +475,16 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   };
   int partial_n = 0;
   const auto fetch_next = [&](int s) __attribute__((always_inline)) {
-    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
+    const int t = s + 3 < n ? s + 3 : n - 1;
+    e3 = sload_issue(pent + (t >> 1));  // lands at the end of the VALU phase
+    partial_n = s + 1 < n ? needs_mask(e1) : 0;
   };
   const auto land_next = [&]() __attribute__((always_inline)) {
+    sload_wait(e3);
     asm volatile("" ::"s"(partial_n));
+    e1 = e2;
+    e2 = e3;
   };
-  const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
   // Loads of step s: K(s + 2) and its ids (group A, 5 per wave), V(s + 2)
   // (group B, 4 per wave), issued at the start of the group's VALU phase and
   // waited for at the end of step s + 1 (loads finish in order).
@@ -520,7 +507,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     fence();
     __builtin_amdgcn_s_setprio(0);
     if (K != 1) {
-      const int k0n = k0_of(last_sub(s + 2));
+      const int k0n = k0_of(e2, s + 2);
       const auto rk = rows(k, k0n);
       load_ids(k0n, kload);
 #pragma unroll
@@ -537,7 +524,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                           const char* vcur, char* vload) __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
     if (K != 1) {
-      const auto rv = rows(v, k0_of(last_sub(s + 2)));
+      const auto rv = rows(v, k0_of(e2, s + 2));
 #pragma unroll
       for (int j = 0; j < 4; ++j) load_piece(j, rv, vload);
     }
@@ -556,7 +543,7 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   using Mid = std::integral_constant<int, 2>;
   // prologue: K(0), K(1) (group A), V(0), V(1) (group B)
   if (n > 0) {
-    const int k00 = k0_of(0), k01 = k0_of(last_sub(1));
+    const int k00 = k0_of(ent(0), 0), k01 = k0_of(e1, 1);
     if (grp == 0) {
       const auto r0 = rows(k, k00), r1 = rows(k, k01);
       load_ids(k00, kb0);
@@ -857,25 +844,32 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   bf16x8 ob[4];  // P (P wave) or dS (D wave) as MFMA operands, 16 queries each
   char* const xb = xch + wq * 4096;
 
-  // per-step scalars, fetched a step ahead in a VALU phase (an outstanding
-  // scalar load would force every LDS operand wait of an MFMA phase to zero)
+  // Per-step scalars, fetched a step ahead in a VALU phase (an outstanding
+  // scalar load would force every LDS operand wait of an MFMA phase to zero):
+  // at step s, qt_l is the query tile of sub-step s + 2 (the one this step
+  // loads) and qt_p that of s + 1; the step issues the loads of the query tile
+  // of s + 3 and of the class word of (qt_p, kt) -- independent of each other,
+  // both landed at the end of the VALU phase.
   const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
   const auto qt_of = [&](int s) { return kv_rows[beg + (last_sub(s) >> 1)]; };
   const auto q0_of = [&](int s, int qt) { return qt * 128 + 64 * (last_sub(s) & 1); };
-  const auto needs_mask = [&](int s) {
-    return tile_class_at(tile_class, (size_t)qt_of(s) * nkt + kt) != 2;
-  };
-  int qt_l = n > 0 ? qt_of(2) : 0;  // query tile of the sub-tile this step loads
-  bool partial_c = n > 0 && needs_mask(0);
-  int qt_nl = 0, partial_n = 0;
+  int qt_l = n > 0 ? qt_of(2) : 0, qt_p = n > 0 ? qt_of(1) : 0;
+  bool partial_c = n > 0 && tile_class_at(tile_class, (size_t)qt_of(0) * nkt + kt) != 2;
+  int qt_nl = 0, partial_n = 0, cword = 0, csh = 0, s_next = 0;
   const auto fetch_next = [&](int s) __attribute__((always_inline)) {
-    qt_nl = qt_of(s + 3);
-    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
+    qt_nl = sload_issue(kv_rows + beg + (last_sub(s + 3) >> 1));
+    const size_t idx = (size_t)qt_p * nkt + kt;
+    cword = sload_issue((const int32_t*)tile_class + (idx >> 2));
+    csh = 8 * (int)(idx & 3);
+    s_next = s + 1;
   };
   const auto land_next = [&]() __attribute__((always_inline)) {
+    sload_wait2(qt_nl, cword);
+    partial_n = s_next < n ? (((cword >> csh) & 0xFF) != 2) : 0;
     asm volatile("" ::"s"(qt_nl), "s"(partial_n));
   };
   const auto rotate = [&]() __attribute__((always_inline)) {
+    qt_p = qt_l;
     qt_l = qt_nl;
     partial_c = partial_n;
   };
@@ -1153,7 +1147,6 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     const int q0 = q0_of(s + 2, qt_l);
     constexpr int nbat = K == 2 ? 8 : 4;
     if (K != 1) load_one(0, 0, q0, ld);
-    fetch_next(s);
     if (K != 0) {
       ds_phase([&]() __attribute__((always_inline)) {
         if (K != 1) load_one(1, 0, q0, ld);
@@ -1162,6 +1155,9 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     } else {
       load_one(1, 0, q0, ld);
     }
+    // after the hand-over's LDS accesses, whose waits would otherwise also
+    // wait for these scalar loads
+    fetch_next(s);
     if (K != 1) load_words(q0, ld);
     prefetch(kind, prev, cur + kSpSub);
     pin_ob();
@@ -1416,9 +1412,8 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
     if (bf && D == 128)                                                                          \
       hipLaunchKernelGGL(dq_bf16_pair_kernel<128>, gq2, dim3(512), 0, s, (const uint16_t*)q,     \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
-                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale,                   \
-                         mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,             \
-                         mask->nkv_tiles, (uint16_t*)dq);                                        \
+                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale, mask->q_order,    \
+                         mask->pair_off, mask->pair_len, mask->pair_ent, (uint16_t*)dq);         \
     else if (bf)                                                                                 \
       hipLaunchKernelGGL(dq_bf16_kernel<D>, gq, dim3(256), 0, s, (const uint16_t*)q,             \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \

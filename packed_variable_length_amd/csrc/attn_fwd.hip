@@ -152,7 +152,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * s2;
+    mx = half_max(mx) * s2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
@@ -195,7 +195,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 
   // epilogue: both half-waves hold partial sums of the same query
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float ltot = half_sum(lsum);
   const bool any = ltot > 0.f;
   const float inv = any ? 1.f / ltot : 0.f;
   if (qin) {
@@ -223,10 +223,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // softmax; B: softmax then MFMA phase; one workgroup barrier per step, at its
 // end), so each K/V sub-tile staged in LDS
 // serves 256 query rows: half the staging traffic per flop of one tile per
-// workgroup.  The sub-tiles cover each tile's key-tile range [first, last] of
-// its list -- one range when the two overlap or touch, else both ranges one
-// after the other; a tile in the walk that is not in a group's list is fully
-// masked for that group (class 0).
+// workgroup.  The sub-tiles walk the pair's list of the block mask: the key
+// tiles one of the two query tiles has work with, ascending; a tile in the
+// walk that is not in a group's list is fully masked for that group (class 0).
 constexpr int kPrSub = 64 * kRowBytes;  // one 64-key sub-tile (16 KB)
 
 template <int D>
@@ -234,10 +233,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const int32_t* __restrict__ q_ids,
                      const int32_t* __restrict__ kv_ids, int32_t nq, int32_t nkv, int32_t H,
-                     float s2, const uint8_t* __restrict__ tile_class,
-                     const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ q_cols,
-                     const int32_t* __restrict__ q_order, int32_t nkt,
-                     uint16_t* __restrict__ o, float* __restrict__ lse) {
+                     float s2, const int32_t* __restrict__ q_order,
+                     const int32_t* __restrict__ pair_off, const int32_t* __restrict__ pair_len,
+                     const int32_t* __restrict__ pair_ent, uint16_t* __restrict__ o,
+                     float* __restrict__ lse) {
   static_assert(D == 128, "the paired forward is laid out for 128-wide heads");
   constexpr int kDB = D / 32, kKK = D / 16;
   __shared__ __attribute__((aligned(1024))) char kb0[kPrSub + 256];
@@ -255,34 +254,11 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   block_work(blockIdx.x, H, (nqt + 1) / 2, &work, &h);
   const int qpair[2] = {q_order[2 * work], 2 * work + 1 < nqt ? q_order[2 * work + 1] : -1};
   const int qmine = qpair[grp];  // -1: no tile (odd tile count), no rows, all masked
-  // key-tile ranges of the two lists (empty: first > last)
-  int first[2], last[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    first[g] = INT_MAX;
-    last[g] = -1;
-    if (qpair[g] >= 0 && q_ptr[qpair[g] + 1] > q_ptr[qpair[g]]) {
-      first[g] = q_cols[q_ptr[qpair[g]]];
-      last[g] = q_cols[q_ptr[qpair[g] + 1] - 1];
-    }
-  }
-  // the walk: segment 0 = [lo0, lo0 + len0), then segment 1 = [lo1, lo1 + len1)
-  int lo0, len0, lo1 = 0, len1 = 0;
-  if (last[1] < 0 || (last[0] >= 0 && first[1] <= last[0] + 1 && first[0] <= last[1] + 1)) {
-    lo0 = min(first[0], first[1]);  // one range (or only one list)
-    len0 = max(last[0], last[1]) - lo0 + 1;
-  } else if (last[0] < 0) {
-    lo0 = first[1];
-    len0 = last[1] - first[1] + 1;
-  } else {
-    const int g0 = first[0] <= first[1] ? 0 : 1;
-    lo0 = first[g0];
-    len0 = last[g0] - first[g0] + 1;
-    lo1 = first[1 - g0];
-    len1 = last[1 - g0] - first[1 - g0] + 1;
-  }
-  if (len0 < 0) len0 = 0;  // both lists empty
-  const int n = 2 * (len0 + len1);  // 64-key sub-steps
+  // The key walk: the pair's list from the block mask -- every key tile one of
+  // the two query tiles has an allowed pair with, ascending, each entry the key
+  // tile with both tiles' classes beside it; two 64-key sub-steps per tile.
+  const int32_t* const pent = pair_ent + pair_off[work];
+  const int n = 2 * pair_len[work];
   const size_t rs = (size_t)H * D;
   const int hoff = h * D;
 
@@ -308,17 +284,25 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   f32x16 sacc[2];
   bf16x8 pb[4];
 
-  // first key row of sub-step s; whether sub-step s needs the id mask for
-  // this group's tile (not a full tile: partial, or empty = all masked)
-  const auto tile_of = [&](int s) {
-    const int u = s >> 1;
-    return u < len0 ? lo0 + u : lo1 + (u - len0);
+  // Walk entries as scalars: ent(s) is the entry of sub-step s (clamped to the
+  // last one); the first key row of sub-step s comes from its entry, and the id
+  // mask is needed unless this group's tile is full for that key tile (class 2;
+  // partial, empty or no tile at all need it).  e1, e2 hold the entries of
+  // sub-steps s + 1 and s + 2 at step s; the entry of s + 3 is fetched during
+  // the step's VALU phase and waited for only at its end.
+  const auto ent = [&](int s) { return pent[(s < n ? s : n - 1) >> 1]; };
+  const auto k0_of = [&](int e, int s) {
+    return (e & 0xFFFF) * 128 + 64 * ((s < n ? s : n - 1) & 1);
   };
-  const auto k0_of = [&](int s) { return tile_of(s) * 128 + 64 * (s & 1); };
-  const auto needs_mask = [&](int s) {
-    return qmine < 0 || tile_class_at(tile_class, (size_t)qmine * nkt + tile_of(s)) != 2;
-  };
-  bool partial_c = n > 0 && needs_mask(0);
+  const int csh = 16 + 8 * grp;
+  const auto needs_mask = [&](int e) { return ((e >> csh) & 0xFF) != 2; };
+  int e1 = 0, e2 = 0, e3 = 0;
+  bool partial_c = false;
+  if (n > 0) {
+    partial_c = needs_mask(ent(0));
+    e1 = ent(1);
+    e2 = ent(2);
+  }
 
   // Group A stages the K sub-tiles (and their ids, by wave 0), group B the V
   // sub-tiles: 16 row groups over a group's four waves (row groups wq + 4 j,
@@ -422,7 +406,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * s2;
+    mx = half_max(mx) * s2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
@@ -470,10 +454,15 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   int partial_n = 0;
   const auto fetch_next = [&](int s) __attribute__((always_inline)) {
-    partial_n = s + 1 < n ? needs_mask(s + 1) : 0;
+    const int t = s + 3 < n ? s + 3 : n - 1;
+    e3 = sload_issue(pent + (t >> 1));  // lands at the end of the VALU phase
+    partial_n = s + 1 < n ? needs_mask(e1) : 0;
   };
   const auto land_next = [&]() __attribute__((always_inline)) {
+    sload_wait(e3);
     asm volatile("" ::"s"(partial_n));
+    e1 = e2;
+    e2 = e3;
   };
   // Three buffers each for K and V: sub-tile s sits in kb[s % 3] / vb[s % 3].
   // Step s stages K(s + 2) (group A) and V(s + 1) (group B), each group at the
@@ -481,7 +470,6 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // loads at the end of step s + 1, so a load has two steps to land.  Past the
   // last sub-tile the loads re-read sub-tile n - 1 into the free buffer, which
   // keeps the per-step load count (and so the partial waits) fixed.
-  const auto last_sub = [&](int s) { return s < n ? s : n - 1; };
   // Each wave of group A stages 16 of the sub-tile's 64 key ids (one load
   // with 16 active lanes), so every wave of a group issues the same number of
   // loads per step.  A sub-tile inside the keys takes the buffer form; the
@@ -520,7 +508,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     mfma_phase(kind, kcur, vprev, partial_c);
     fence();
     if (K != 1) {
-      const int k0n = k0_of(last_sub(s + 2));
+      const int k0n = k0_of(e2, s + 2);
       const auto rk = rows(k, k0n);
       load_ids(k0n, kload);
 #pragma unroll
@@ -538,7 +526,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                           __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
     if (K != 1) {
-      const auto rv = rows(v, k0_of(last_sub(s + 1)));
+      const auto rv = rows(v, k0_of(e1, s + 1));
 #pragma unroll
       for (int j = 0; j < 4; ++j) load_piece(j, rv, vload);
     }
@@ -557,7 +545,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // prologue: K(0) -> kb0, K(1) -> kb1 (group A), V(0) -> vb0 (group B)
   if (n > 0) {
     if (grp == 0) {
-      const int k00 = k0_of(0), k01 = k0_of(last_sub(1));
+      const int k00 = k0_of(ent(0), 0), k01 = k0_of(e1, 1);
       const auto r0 = rows(k, k00), r1 = rows(k, k01);
       load_ids(k00, kb0);
       load_ids(k01, kb1);
@@ -567,7 +555,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         load_piece(j, r1, kb1);
       }
     } else {
-      const auto r0 = rows(v, k0_of(0));
+      const auto r0 = rows(v, k0_of(ent(0), 0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) load_piece(j, r0, vb0);
     }
@@ -597,7 +585,7 @@ fwd_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float ltot = half_sum(lsum);
   const bool any = ltot > 0.f;
   const float inv = any ? 1.f / ltot : 0.f;
   if (qin) {
@@ -703,7 +691,7 @@ int32_t check_attn_args(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, i
     if (!ok(mask->block_q) || !ok(mask->block_kv)) return PA_ERR_MASK_MISMATCH;
   }
   if (!mask->tile_class || !mask->q_ptr || !mask->q_cols || !mask->kv_ptr || !mask->kv_rows ||
-      !mask->q_order || !mask->kv_order)
+      !mask->q_order || !mask->kv_order || !mask->pair_off || !mask->pair_len || !mask->pair_ent)
     return PA_ERR_NULL;
   if ((int64_t)mask->nq_tiles * heads > INT32_MAX || (int64_t)mask->nkv_tiles * heads > INT32_MAX)
     return PA_ERR_SHAPE;
@@ -730,8 +718,8 @@ extern "C" int32_t attn_packed_fwd(int32_t dtype, int32_t nq, int32_t nkv, int32
       hipLaunchKernelGGL(fwd_bf16_pair_kernel<128>, dim3((mask->nq_tiles + 1) / 2 * heads),
                          dim3(512), 0, s, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, q_seq_id, kv_seq_id, nq, nkv,
-                         heads, s2, mask->tile_class, mask->q_ptr, mask->q_cols, mask->q_order,
-                         mask->nkv_tiles, (uint16_t*)o, lse);
+                         heads, s2, mask->q_order, mask->pair_off, mask->pair_len,
+                         mask->pair_ent, (uint16_t*)o, lse);
     else
       hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, q_seq_id, kv_seq_id, nq, nkv,

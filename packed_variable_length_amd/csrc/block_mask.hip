@@ -20,6 +20,12 @@
 //   5. scan_sort     two blocks: exclusive scan of the counts into CSR row
 //                    pointers, and a bitonic sort giving the longest-first order.
 //   6. compact       one block per row: ascending column lists via wave ballots.
+//   7. pair_compact  one block per pair of query tiles (positions 2w, 2w+1 of the
+//                    longest-first order, the pairs the paired attention kernels
+//                    run): the ascending union of the two key-tile lists, each
+//                    entry the key tile with both tiles' classes packed beside it,
+//                    so those kernels walk exactly the key tiles one of the two
+//                    query tiles needs.
 #include "pa_common.h"
 
 namespace {
@@ -211,7 +217,7 @@ __global__ void __launch_bounds__(kSortThreads)
 scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ cnt_kv,
                  int32_t nqt, int32_t nkt, int32_t* __restrict__ q_ptr,
                  int32_t* __restrict__ kv_ptr, int32_t* __restrict__ q_order,
-                 int32_t* __restrict__ kv_order) {
+                 int32_t* __restrict__ kv_order, int32_t* __restrict__ pair_off) {
   __shared__ uint32_t keys[kMaxTiles];
   __shared__ int32_t partial[kSortThreads];
   const bool qside = blockIdx.x == 0;
@@ -265,6 +271,34 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
     }
   }
   for (int i = t; i < n; i += kSortThreads) order[i] = (int32_t)(keys[i] % (uint32_t)n);
+  if (!qside) return;
+
+  // query side: room for each pair's union list (the sum of its two list
+  // lengths, an upper bound), as an exclusive scan over the pairs
+  const int np = (n + 1) / 2;
+  const int pchunk = (np + kSortThreads - 1) / kSortThreads;
+  const int p0 = t * pchunk, p1 = min(np, p0 + pchunk);
+  const auto cap = [&](int w) {
+    const int a = (int)(keys[2 * w] % (uint32_t)n);
+    return cnt[a] + (2 * w + 1 < n ? cnt[(int)(keys[2 * w + 1] % (uint32_t)n)] : 0);
+  };
+  int plocal = 0;
+  for (int w = p0; w < p1; ++w) plocal += cap(w);
+  __syncthreads();
+  partial[t] = plocal;
+  __syncthreads();
+  for (int o = 1; o < kSortThreads; o <<= 1) {
+    const int v = t >= o ? partial[t - o] : 0;
+    __syncthreads();
+    partial[t] += v;
+    __syncthreads();
+  }
+  int prun = partial[t] - plocal;
+  for (int w = p0; w < p1; ++w) {
+    pair_off[w] = prun;
+    prun += cap(w);
+  }
+  if (t == kSortThreads - 1) pair_off[np] = partial[t];
 }
 
 // ---------------------------------------------------------------- 6. compact
@@ -297,9 +331,44 @@ compact_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_
   }
 }
 
+// ---------------------------------------------------------------- 7. pair lists
+// Block w: query tiles a = q_order[2w] and b = q_order[2w + 1] (none past the
+// end).  Entry = key tile | class(a, kt) << 16 | class(b, kt) << 24 for every
+// key tile at least one of the two rows has an allowed pair with, ascending.
+__global__ void __launch_bounds__(256)
+pair_compact_kernel(const uint8_t* __restrict__ cls, int32_t nqt, int32_t nkt,
+                    const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
+                    int32_t* __restrict__ pair_len, int32_t* __restrict__ pair_ent) {
+  __shared__ int wave_tot[4];
+  const int w = blockIdx.x;
+  const int a = q_order[2 * w];
+  const int b = 2 * w + 1 < nqt ? q_order[2 * w + 1] : -1;
+  const uint8_t* ra = cls + (size_t)a * nkt;
+  const uint8_t* rb = b >= 0 ? cls + (size_t)b * nkt : nullptr;
+  int32_t* dst = pair_ent + pair_off[w];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int base = 0;
+  for (int j0 = 0; j0 < nkt; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const int ca = j < nkt ? ra[j] : 0;
+    const int cb = (j < nkt && rb) ? rb[j] : 0;
+    const bool nz = (ca | cb) != 0;
+    const uint64_t m = __ballot(nz);
+    if (lane == 0) wave_tot[wv] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int x = 0; x < wv; ++x) off += wave_tot[x];
+    if (nz) dst[off + __popcll(m & lt)] = j | (ca << 16) | (cb << 24);
+    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) pair_len[w] = base;
+}
+
 struct Layout {
   size_t cls, cls_t, q_ptr, kv_ptr, q_order, kv_order, q_cols, kv_rows, q_sum, kv_sum, cnt_q,
-      cnt_kv, queue, queue_count, total;
+      cnt_kv, queue, queue_count, pair_off, pair_len, pair_ent, total;
 };
 
 bool make_layout(int32_t nq, int32_t nkv, int32_t bq, int32_t bkv, Layout* L, int32_t* nqt_out,
@@ -328,6 +397,10 @@ bool make_layout(int32_t nq, int32_t nkv, int32_t bq, int32_t bkv, Layout* L, in
   L->cnt_kv = take(nkt * 4);
   L->queue = take(pairs * 4);
   L->queue_count = take(4);
+  const size_t npairs = (size_t)(nqt + 1) / 2;
+  L->pair_off = take((npairs + 1) * 4);
+  L->pair_len = take(npairs * 4);
+  L->pair_ent = take(pairs * 4);
   L->total = off;
   *nqt_out = (int32_t)nqt;
   *nkt_out = (int32_t)nkt;
@@ -369,6 +442,9 @@ extern "C" int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const i
   int32_t* cnt_kv = (int32_t*)(base + L.cnt_kv);
   int32_t* queue = (int32_t*)(base + L.queue);
   int32_t* queue_count = (int32_t*)(base + L.queue_count);
+  int32_t* pair_off = (int32_t*)(base + L.pair_off);
+  int32_t* pair_len = (int32_t*)(base + L.pair_len);
+  int32_t* pair_ent = (int32_t*)(base + L.pair_ent);
 
   const int waves = nqt + nkt;
   hipLaunchKernelGGL(tile_summary_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, q_seq_id, nq,
@@ -382,9 +458,11 @@ extern "C" int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const i
   hipLaunchKernelGGL(count_kernel, dim3(nqt + nkt), dim3(256), 0, s, cls, cls_t, nqt, nkt, cnt_q,
                      cnt_kv);
   hipLaunchKernelGGL(scan_sort_kernel, dim3(2), dim3(kSortThreads), 0, s, cnt_q, cnt_kv, nqt, nkt,
-                     q_ptr, kv_ptr, q_order, kv_order);
+                     q_ptr, kv_ptr, q_order, kv_order, pair_off);
   hipLaunchKernelGGL(compact_kernel, dim3(nqt + nkt), dim3(256), 0, s, cls, cls_t, nqt, nkt, q_ptr,
                      kv_ptr, q_cols, kv_rows);
+  hipLaunchKernelGGL(pair_compact_kernel, dim3((nqt + 1) / 2), dim3(256), 0, s, cls, nqt, nkt,
+                     q_order, pair_off, pair_len, pair_ent);
   const int32_t st = pa::launch_status();
   if (st != PA_OK) return st;
   out->nq = nq;
@@ -400,5 +478,8 @@ extern "C" int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const i
   out->kv_rows = kv_rows;
   out->q_order = q_order;
   out->kv_order = kv_order;
+  out->pair_off = pair_off;
+  out->pair_len = pair_len;
+  out->pair_ent = pair_ent;
   return PA_OK;
 }

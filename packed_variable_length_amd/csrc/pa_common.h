@@ -40,6 +40,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// A lane's value and that of lane l ^ 32 (the other half of the wave) from one
+// v_permlane32_swap -- a VALU op, no LDS round trip.  Swapping a register with
+// itself leaves (own, other) in the two results, in an order that depends on
+// the half, so a symmetric reduction of the pair needs no select.
+__device__ __forceinline__ f32x2 half_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float half_max(float v) {
+  const f32x2 p = half_pair(v);
+  return fmaxf(p[0], p[1]);
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const f32x2 p = half_pair(v);
+  return p[0] + p[1];
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 

@@ -159,6 +159,23 @@ __device__ __forceinline__ int tile_class_at(const uint8_t* __restrict__ cls, si
   return (int)((w >> (8 * (idx & 3))) & 0xFFu);
 }
 
+// A uniform 32-bit load issued where it stands (s_load_dword from inline
+// assembly: the compiler would otherwise sink it to its first use) and landed
+// by sload_wait, which the value is tied to, so nothing reads it earlier.  The
+// compiler does not count this load; its own lgkmcnt waits stay correct (they
+// can only wait longer while it is in flight).  `p` must be 4-byte aligned.
+__device__ __forceinline__ int32_t sload_issue(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void sload_wait(int32_t& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v)::"memory");
+}
+__device__ __forceinline__ void sload_wait2(int32_t& a, int32_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(a), "+s"(b)::"memory");
+}
+
 // Wait for this wave's outstanding direct-to-LDS loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 

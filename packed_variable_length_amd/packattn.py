@@ -49,6 +49,8 @@ class PaBlockMask(ctypes.Structure):
         ("q_ptr", ctypes.c_void_p), ("q_cols", ctypes.c_void_p),
         ("kv_ptr", ctypes.c_void_p), ("kv_rows", ctypes.c_void_p),
         ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p),
+        ("pair_off", ctypes.c_void_p), ("pair_len", ctypes.c_void_p),
+        ("pair_ent", ctypes.c_void_p),
     ]
 
 
@@ -199,6 +201,17 @@ class BlockMask:
         d = self.desc
         return (self._view(d.q_order, d.nq_tiles, torch.int32),
                 self._view(d.kv_order, d.nkv_tiles, torch.int32))
+
+    def pairs(self):
+        """``(pair_off [npairs + 1], pair_len [npairs], pair_ent)`` as device views
+        (entries up to pair_off[-1], the room reserved; a pair's list is
+        pair_ent[off : off + len])."""
+        d = self.desc
+        npairs = (d.nq_tiles + 1) // 2
+        off = self._view(d.pair_off, npairs + 1, torch.int32)
+        total = int(off[-1].item())
+        return (off, self._view(d.pair_len, npairs, torch.int32),
+                self._view(d.pair_ent, total, torch.int32))
 
 
 def build_block_mask_bytes(nq: int, nkv: int, block_q: int = 128, block_kv: int = 128) -> int:

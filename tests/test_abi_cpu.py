@@ -99,7 +99,8 @@ def _fake_mask(nq, nkv, bq=128, bkv=128):
     d = PaBlockMask()
     d.nq, d.nkv, d.block_q, d.block_kv = nq, nkv, bq, bkv
     d.nq_tiles, d.nkv_tiles = -(-nq // bq), -(-nkv // bkv)
-    for f in ("tile_class", "q_ptr", "q_cols", "kv_ptr", "kv_rows", "q_order", "kv_order"):
+    for f in ("tile_class", "q_ptr", "q_cols", "kv_ptr", "kv_rows", "q_order", "kv_order",
+              "pair_off", "pair_len", "pair_ent"):
         setattr(d, f, 0x200000)
     return d
 

@@ -47,16 +47,21 @@ def _check_mask(pa, qid, kid, bq, bkv):
     wq_ptr, wq_cols, wkv_ptr, wkv_rows = obm.csr_lists(want)
     assert np.array_equal(q_ptr, wq_ptr) and np.array_equal(q_cols, wq_cols)
     assert np.array_equal(kv_ptr, wkv_ptr) and np.array_equal(kv_rows, wkv_rows)
-    # longest-first orders: a permutation, lengths non-increasing, ties ascending
+    # longest-first orders (ties ascending: unique) and the pair walks
     q_order, kv_order = (t.cpu().numpy() for t in m.orders())
-    for order, ptr in ((q_order, q_ptr), (kv_order, kv_ptr)):
-        n = len(ptr) - 1
-        assert sorted(order.tolist()) == list(range(n))
-        lens = np.diff(ptr)[order]
-        assert (np.diff(lens) <= 0).all()
-        tie = lens[:-1] == lens[1:]
-        assert (order[:-1][tie] < order[1:][tie]).all()
+    assert np.array_equal(q_order, obm.longest_first_order(want, 0))
+    assert np.array_equal(kv_order, obm.longest_first_order(want, 1))
+    _check_pairs(m, want, q_order)
     return cls
+
+
+def _check_pairs(m, want, q_order):
+    off, ln, ent = (t.cpu().numpy() for t in m.pairs())
+    room, lists = obm.pair_lists(want, q_order)
+    assert np.array_equal(off, room)
+    assert np.array_equal(ln, [len(x) for x in lists])
+    for w, x in enumerate(lists):
+        assert np.array_equal(ent[off[w]:off[w] + ln[w]], x), f"pair {w}"
 
 
 def test_mask_closed_form_totals(pa):
@@ -115,3 +120,6 @@ def test_mask_stress_1m_tokens(pa):
     wq_ptr, wq_cols, wkv_ptr, wkv_rows = obm.csr_lists(want)
     assert np.array_equal(q_ptr, wq_ptr) and np.array_equal(q_cols, wq_cols)
     assert np.array_equal(kv_ptr, wkv_ptr) and np.array_equal(kv_rows, wkv_rows)
+    q_order = m.orders()[0].cpu().numpy()
+    assert np.array_equal(q_order, obm.longest_first_order(want, 0))
+    _check_pairs(m, want, q_order)

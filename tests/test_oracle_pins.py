@@ -162,6 +162,44 @@ def _golden_totals(golden_dir):
     return rows
 
 
+def test_blockmask_order_and_pair_lists_hand_worked():
+    """Orders and pair walks of a hand-made class matrix (3 query x 4 key tiles):
+    row lengths 2, 3, 2 -> query order 1, 0, 2 (ties by index); key-tile column
+    lengths 2, 2, 1, 2 -> key order 0, 1, 3, 2.  Pair 0 = tiles (1, 0): union of
+    {0, 1, 3} and {0, 2} = 0, 1, 2, 3; pair 1 = tile 2 alone: {1, 3}."""
+    cls = np.array([[2, 0, 1, 0],
+                    [1, 2, 0, 1],
+                    [0, 1, 0, 2]], dtype=np.uint8)
+    assert obm.longest_first_order(cls, 0).tolist() == [1, 0, 2]
+    assert obm.longest_first_order(cls, 1).tolist() == [0, 1, 3, 2]
+    room, lists = obm.pair_lists(cls, np.array([1, 0, 2]))
+    assert room.tolist() == [0, 5, 7]
+    e = lambda kt, a, b: kt | (a << 16) | (b << 24)  # noqa: E731
+    assert lists[0].tolist() == [e(0, 1, 2), e(1, 2, 0), e(2, 0, 1), e(3, 1, 0)]
+    assert lists[1].tolist() == [e(1, 1, 0), e(3, 2, 0)]
+
+
+def test_blockmask_pair_lists_cover_both_lists(seed=7):
+    """Each pair's walk is exactly the sorted union of its two tiles' CSR lists,
+    and the classes beside each entry are the class matrix entries."""
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        nqt, nkt = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        cls = rng.choice(np.array([0, 0, 1, 2], np.uint8), size=(nqt, nkt))
+        order = obm.longest_first_order(cls, 0)
+        q_ptr, q_cols, _, _ = obm.csr_lists(cls)
+        room, lists = obm.pair_lists(cls, order)
+        for w, x in enumerate(lists):
+            tiles = [int(order[2 * w])] + ([int(order[2 * w + 1])] if 2 * w + 1 < nqt else [])
+            union = sorted(set().union(*[q_cols[q_ptr[t]:q_ptr[t + 1]].tolist() for t in tiles]))
+            assert [v & 0xFFFF for v in x.tolist()] == union
+            for v in x.tolist():
+                kt = v & 0xFFFF
+                assert (v >> 16) & 0xFF == cls[tiles[0], kt]
+                assert (v >> 24) & 0xFF == (cls[tiles[1], kt] if len(tiles) > 1 else 0)
+            assert room[w + 1] - room[w] == sum(q_ptr[t + 1] - q_ptr[t] for t in tiles)
+
+
 def test_blockmask_closed_form_totals(golden_dir):
     by_name = {wl.config(i).name: wl.config(i) for i in (1, 2, 3)}
     for name, bq, bkv, want in _golden_totals(golden_dir):
