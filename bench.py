@@ -331,7 +331,7 @@ def _useful_pairs(q_ids, kv_ids):
                 np.bincount(kv, minlength=m).astype(np.int64)).sum())
 
 
-STAGES = ["seq_ids", "block_mask", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv"]
+STAGES = ["seq_ids", "block_mask", "fwd", "bwd_dq", "bwd_dkdv"]  # bwd_dq includes the row terms
 
 
 class PackStep:
@@ -392,14 +392,12 @@ class PackStep:
         pa.attn_packed_fwd(self.Q, self.K, self.V, self.qids, self.kids, mask, s.scale,
                            out=self.O, lse=self.lse)
         mark(3)
-        pa.attn_packed_bwd_preprocess(self.O, self.DO, self.lse, self.ws)
+        pa.attn_packed_bwd_dq(self.Q, self.K, self.V, self.O, self.DO, self.lse, self.ws,
+                              self.qids, self.kids, mask, s.scale, dq=self.dQ)
         mark(4)
-        pa.attn_packed_bwd_dq(self.Q, self.K, self.V, self.DO, self.lse, self.ws, self.qids,
-                              self.kids, mask, s.scale, dq=self.dQ)
-        mark(5)
         pa.attn_packed_bwd_dkdv(self.Q, self.K, self.V, self.DO, self.lse, self.ws, self.qids,
                                 self.kids, mask, s.scale, dk=self.dK, dv=self.dV)
-        mark(6)
+        mark(5)
 
     def pairs(self):
         import torch
@@ -411,14 +409,15 @@ def time_steps(step, iters):
     """(mean ms per step, mean ms per stage) from HIP events on the library's stream."""
     import numpy as np
     import torch
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(iters)]
+    ne = len(STAGES) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in range(iters)]
     torch.cuda.synchronize()
     for i in range(iters):
         step(evs[i])
     torch.cuda.synchronize()
     stage = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, n in enumerate(STAGES)}
-    total = float(np.mean([e[0].elapsed_time(e[6]) for e in evs]))
+    total = float(np.mean([e[0].elapsed_time(e[ne - 1]) for e in evs]))
     return total, stage
 
 

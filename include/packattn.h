@@ -230,19 +230,25 @@ int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads, i
                         void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages attn_packed_bwd runs, callable one by one (same kernels,
- * same results; for callers that time or overlap the stages).  `workspace` is
- * a device buffer of >= attn_packed_bwd_workspace_bytes(...) bytes, 256-byte
- * aligned, that the preprocess fills and the other two stages read.
+ * The two stages attn_packed_bwd runs, callable one by one (same kernels,
+ * same results; for callers that time or overlap the stages), and the row
+ * terms alone.  `workspace` is a device buffer of >=
+ * attn_packed_bwd_workspace_bytes(...) bytes, 256-byte aligned.
  *
- * attn_packed_bwd_preprocess -- the row terms of the softmax gradient:
- *   Delta[h][i] = sum_d dout[i][h][d] * o[i][h][d] (fp32) and the forward's LSE
- *   in log2 units (+inf on rows without an allowed key, so that P = 0 there).
+ * attn_packed_bwd_preprocess -- the row terms of the softmax gradient alone,
+ *   into the workspace: Delta[h][i] = sum_d dout[i][h][d] * o[i][h][d] (fp32)
+ *   and the forward's LSE in log2 units (+inf on rows without an allowed key,
+ *   so that P = 0 there).  attn_packed_bwd does not need it (its dQ stage
+ *   computes the same terms); it serves callers that want them alone.
  *   Errors: PA_ERR_DTYPE, PA_ERR_HEADDIM, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
  *           PA_ERR_WORKSPACE, PA_ERR_HIP.
- * attn_packed_bwd_dq -- dq = scale * dS K, one workgroup per query tile.
+ * attn_packed_bwd_dq -- the row terms (written to the workspace, as by the
+ *   preprocess; with bf16 and 128-wide heads the dQ kernel computes them from
+ *   o and dout itself, otherwise the preprocess kernel runs first) and
+ *   dq = scale * dS K, query tile by query tile.
  * attn_packed_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dout, one workgroup
- *   per key tile.
+ *   per key tile; reads the row terms a dQ stage (or the preprocess) on the
+ *   same inputs wrote into the workspace.
  *   Both: arguments and errors as attn_packed_bwd.
  */
 int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t heads, int32_t head_dim,
@@ -250,8 +256,8 @@ int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t heads, int
                                    void* workspace, size_t workspace_bytes, void* stream);
 int32_t attn_packed_bwd_dq(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                            int32_t head_dim, float scale, const void* q, const void* k,
-                           const void* v, const void* dout, const float* lse,
-                           const void* workspace, size_t workspace_bytes,
+                           const void* v, const void* o, const void* dout, const float* lse,
+                           void* workspace, size_t workspace_bytes,
                            const int32_t* q_seq_id, const int32_t* kv_seq_id,
                            const pa_block_mask* mask, void* dq, void* stream);
 int32_t attn_packed_bwd_dkdv(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,

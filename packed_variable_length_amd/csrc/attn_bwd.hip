@@ -10,11 +10,13 @@
 // variable length" report, implementation part; "LingBot-VA packing" report,
 // section 2.2); rows with no allowed pair get exact zero gradients.
 //
-// Three launches, none with atomics:
-//   preprocess  Delta = rowsum(dO * O) and LSE in log2 units (+inf on rows
-//               without an allowed key, so exp2 gives P = 0 there); HBM-bound
-//   dq          query-major, one 128-row query tile per workgroup: S^T = K Q^T,
-//               dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (query index on the lanes)
+// Two launches, none with atomics:
+//   dq          query-major: first the row terms of its queries, Delta =
+//               rowsum(dO * O) and LSE in log2 units (+inf on rows without an
+//               allowed key, so exp2 gives P = 0 there), written for dkdv; then
+//               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (query index
+//               on the lanes).  For 64-wide heads and fp32 a separate
+//               HBM-bound preprocess kernel computes the row terms first.
 //   dkdv        key-major, one 128-row key tile per workgroup: S = Q K^T,
 //               P (packed to bf16 at once), dP = dO V^T, dS from the bf16 P,
 //               dV^T += dO^T P, dK^T += Q^T dS (key index on the lanes, dK and
@@ -248,7 +250,8 @@ template <int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                    const float* __restrict__ delta, const float* __restrict__ lse2,
+                    const uint16_t* __restrict__ o, const float* __restrict__ lse,
+                    float* __restrict__ delta, float* __restrict__ lse2,
                     const int32_t* __restrict__ q_ids, const int32_t* __restrict__ kv_ids,
                     int32_t nq, int32_t nkv, int32_t H, float s2, float scale,
                     const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
@@ -285,8 +288,6 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int qc = qin ? qrow : nq - 1;
   const int qid = qin ? q_ids[qrow] : -1;
   const bool qvalid = qid >= 0;
-  const float nl2 = -lse2[(size_t)h * nq + qc];  // -inf on rows without a key: P = 0
-  const float dlt = delta[(size_t)h * nq + qc];
 
   bf16x8 qf[kKK], df[kKK];
   {
@@ -296,6 +297,30 @@ dq_bf16_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     for (int kk = 0; kk < kKK; ++kk) {
       qf[kk] = *(const bf16x8*)(qp + 16 * kk);
       df[kk] = *(const bf16x8*)(dp + 16 * kk);
+    }
+  }
+  // The row terms of the softmax gradient for this lane's query, from its O
+  // and dO rows (the lane holds half of the row; the other half is in lane
+  // l ^ 32): Delta = sum_d dO O (fp32), and the LSE in log2 units (+inf on rows
+  // without an allowed key, so that exp2 gives P = 0).  Written once per query
+  // for the dK/dV stage, which reads them from the workspace.
+  float dlt, nl2;
+  {
+    const uint16_t* op = o + (size_t)qc * rs + hoff + 8 * hi;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      const bf16x8 ov = *(const bf16x8*)(op + 16 * kk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)df[kk][e], (float)ov[e], part);
+    }
+    dlt = half_sum(part);
+    const float l = lse[(size_t)h * nq + qc];
+    const float l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    nl2 = -l2;
+    if (qin && hi == 0) {
+      delta[(size_t)h * nq + qrow] = dlt;
+      lse2[(size_t)h * nq + qrow] = l2;
     }
   }
   const int rb = row_base(lane), tb = tr_base(lane);
@@ -1151,6 +1176,7 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       ds_phase([&]() __attribute__((always_inline)) {
         if (K != 1) load_one(1, 0, q0, ld);
       });
+      pin_ob();    // dS done (and its waits for the P reads) before what follows
       post_xch();  // P of step s - 1 read: the P wave may write that of step s
     } else {
       load_one(1, 0, q0, ld);
@@ -1161,7 +1187,6 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     if (K != 1) load_words(q0, ld);
     prefetch(kind, prev, cur + kSpSub);
     pin_ob();
-    land_next();
     fence();
     __builtin_amdgcn_s_setprio(2);
     // dK (Q^T of s - 1), dP (dO of s); piece 1 of s + 2 issued between MFMAs
@@ -1170,6 +1195,9 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       if (K != 1 && i == nbat - 2) load_one(1, 1, q0, ld);
     });
     if (K != 1) read_words(cur, kSpDelta);  // Delta of s, for dS in the next step
+    // the scalars land here, after the MFMA phase: their wait (lgkmcnt(0))
+    // placed before it would also drain the prefetched operand reads
+    land_next();
     rotate();
     if (K == 1)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -1391,8 +1419,10 @@ void launch_preprocess(const void* o, const void* dout, const float* lse, int32_
 // through pa_test_set_handover_spin_limit.
 int32_t g_xch_spin_limit = 1 << 20;
 
-// Launches one stage of the backward: 0 = preprocess, 1 = dQ, 2 = dK/dV.
-// `ws` holds Delta [H][nq] followed by LSE*log2(e) [H][nq].
+// Launches one stage of the backward: 0 = the row terms alone (preprocess),
+// 1 = the row terms and dQ (for bf16 128-wide heads one kernel does both), 2 =
+// dK/dV.  `ws` holds Delta [H][nq] followed by LSE*log2(e) [H][nq]; stage 1
+// writes them, stage 2 reads them.
 int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                   int32_t head_dim, float scale, const void* q, const void* k, const void* v,
                   const void* o, const void* dout, const float* lse, const int32_t* q_seq_id,
@@ -1409,11 +1439,18 @@ int32_t bwd_stage(int stage, int32_t dtype, int32_t nq, int32_t nkv, int32_t hea
     if (bf) launch_preprocess<uint16_t, D>(o, dout, lse, nq, heads, delta, lse2, s);             \
     else launch_preprocess<float, D>(o, dout, lse, nq, heads, delta, lse2, s);                   \
   } else if (stage == 1) {                                                                       \
+    /* the paired bf16 kernel computes the row terms itself; the others read */                  \
+    /* them from the workspace, filled by the preprocess first */                                \
+    if (!(bf && D == 128)) {                                                                     \
+      if (bf) launch_preprocess<uint16_t, D>(o, dout, lse, nq, heads, delta, lse2, s);           \
+      else launch_preprocess<float, D>(o, dout, lse, nq, heads, delta, lse2, s);                 \
+    }                                                                                            \
     if (bf && D == 128)                                                                          \
       hipLaunchKernelGGL(dq_bf16_pair_kernel<128>, gq2, dim3(512), 0, s, (const uint16_t*)q,     \
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
-                         lse2, q_seq_id, kv_seq_id, nq, nkv, heads, s2, scale, mask->q_order,    \
-                         mask->pair_off, mask->pair_len, mask->pair_ent, (uint16_t*)dq);         \
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,          \
+                         (const uint16_t*)o, lse, delta, lse2, q_seq_id, kv_seq_id, nq, nkv,     \
+                         heads, s2, scale, mask->q_order, mask->pair_off, mask->pair_len,        \
+                         mask->pair_ent, (uint16_t*)dq);                                         \
     else if (bf)                                                                                 \
       hipLaunchKernelGGL(dq_bf16_kernel<D>, gq, dim3(256), 0, s, (const uint16_t*)q,             \
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, delta,   \
@@ -1500,18 +1537,18 @@ extern "C" int32_t attn_packed_bwd_preprocess(int32_t dtype, int32_t nq, int32_t
 
 extern "C" int32_t attn_packed_bwd_dq(int32_t dtype, int32_t nq, int32_t nkv, int32_t heads,
                                       int32_t head_dim, float scale, const void* q, const void* k,
-                                      const void* v, const void* dout, const float* lse,
-                                      const void* workspace, size_t workspace_bytes,
+                                      const void* v, const void* o, const void* dout,
+                                      const float* lse, void* workspace, size_t workspace_bytes,
                                       const int32_t* q_seq_id, const int32_t* kv_seq_id,
                                       const pa_block_mask* mask, void* dq, void* stream) {
   int32_t st = pa::check_attn_args(dtype, nq, nkv, heads, head_dim, mask);
   if (st != PA_OK) return st;
   if (!lse || !q_seq_id || !kv_seq_id) return PA_ERR_NULL;
-  for (const void* p : {q, k, v, dout, (const void*)dq})
+  for (const void* p : {q, k, v, o, dout, (const void*)dq})
     if ((st = check_tensor(p))) return st;
   if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
-  return bwd_stage(1, dtype, nq, nkv, heads, head_dim, scale, q, k, v, nullptr, dout, lse,
-                   q_seq_id, kv_seq_id, mask, dq, nullptr, nullptr, (float*)workspace,
+  return bwd_stage(1, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse, q_seq_id,
+                   kv_seq_id, mask, dq, nullptr, nullptr, (float*)workspace,
                    (hipStream_t)stream);
 }
 
@@ -1547,7 +1584,7 @@ extern "C" int32_t attn_packed_bwd(int32_t dtype, int32_t nq, int32_t nkv, int32
     if ((st = check_tensor(p))) return st;
   if ((st = check_workspace(workspace, workspace_bytes, dtype, nq, heads, head_dim))) return st;
   const hipStream_t s = (hipStream_t)stream;
-  for (int stage = 0; stage < 3; ++stage) {
+  for (int stage = 1; stage < 3; ++stage) {  // row terms + dQ, then dK/dV
     st = bwd_stage(stage, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse,
                    q_seq_id, kv_seq_id, mask, dq, dk, dv, (float*)workspace, s);
     if (st != PA_OK) return st;
@@ -1606,7 +1643,7 @@ extern "C" int32_t attn_packed_bwd_noalloc(int32_t dtype, int32_t nq, int32_t nk
   // Every entry of Delta and LSE2 that a later stage reads is written by the
   // preprocess first, so nothing in the array needs clearing between calls.
   const hipStream_t s = (hipStream_t)stream;
-  for (int stage = 0; stage < 3; ++stage) {
+  for (int stage = 1; stage < 3; ++stage) {  // row terms + dQ, then dK/dV
     st = bwd_stage(stage, dtype, nq, nkv, heads, head_dim, scale, q, k, v, o, dout, lse,
                    q_seq_id, kv_seq_id, mask, dq, dk, dv, ws, s);
     if (st != PA_OK) return st;

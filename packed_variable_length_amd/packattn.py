@@ -73,8 +73,8 @@ def _load() -> ctypes.CDLL:
         "attn_packed_bwd": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   pm, vp, vp, vp, vp, sz, vp]),
         "attn_packed_bwd_preprocess": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
-        "attn_packed_bwd_dq": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
-                                     vp, vp, pm, vp, vp]),
+        "attn_packed_bwd_dq": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                     sz, vp, vp, pm, vp, vp]),
         "attn_packed_bwd_dkdv": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
                                        vp, vp, pm, vp, vp, vp]),
         "plan_token_packs": (i32, [vp, i32, ctypes.c_int64, vp, vp]),
@@ -393,16 +393,19 @@ def _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale):
     return nq, nkv, H, d, float(scale)
 
 
-def attn_packed_bwd_dq(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, mask: BlockMask,
+def attn_packed_bwd_dq(q, k, v, o, dout, lse, workspace, q_seq_id, kv_seq_id, mask: BlockMask,
                        scale: Optional[float] = None, dq: Optional[torch.Tensor] = None):
+    """The row terms (into ``workspace``, for attn_packed_bwd_dkdv) and dq."""
     nq, nkv, H, d, scale = _stage_args(q, k, v, dout, lse, workspace, q_seq_id, kv_seq_id, scale)
+    _need(o, "o", q.dtype, q.device, q.shape)
     dq = torch.empty_like(q) if dq is None else dq
     _need(dq, "dq", q.dtype, q.device, q.shape)
     _check(_lib.attn_packed_bwd_dq(_DTYPES[q.dtype], nq, nkv, H, d, scale, q.data_ptr(),
-                                   k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                                   workspace.data_ptr(), workspace.numel(), q_seq_id.data_ptr(),
-                                   kv_seq_id.data_ptr(), ctypes.byref(mask.desc), dq.data_ptr(),
-                                   _stream(q)), "attn_packed_bwd_dq")
+                                   k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                   lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   q_seq_id.data_ptr(), kv_seq_id.data_ptr(),
+                                   ctypes.byref(mask.desc), dq.data_ptr(), _stream(q)),
+           "attn_packed_bwd_dq")
     return dq
 
 

@@ -138,7 +138,7 @@ def test_backward_stage_argument_errors(lib):
 
     def dq(mask, wsb, out=FAKE):
         return lib.attn_packed_bwd_dq(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                      FAKE, wsb, FAKE, FAKE, ctypes.byref(mask), out, None)
+                                      FAKE, FAKE, wsb, FAKE, FAKE, ctypes.byref(mask), out, None)
 
     def dkdv(mask, wsb, out=FAKE):
         return lib.attn_packed_bwd_dkdv(1, 500, 500, 2, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,

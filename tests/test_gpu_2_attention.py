@@ -247,9 +247,11 @@ def test_backward_deterministic_and_mask_hazard(pa):
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_backward_stages_match_the_combined_call(pa, dtype, d):
-    """The three stage entry points (preprocess, dQ, dK/dV) called one by one,
+    """The two stage entry points (row terms + dQ, then dK/dV) called one by one,
     into buffers of their own, give gradients bit-identical to attn_packed_bwd
-    (the same kernels) and within tolerance of the oracle."""
+    (the same kernels) and within tolerance of the oracle; the row terms the dQ
+    stage writes agree with the preprocess entry point's, and dK/dV from the
+    preprocess's row terms is within tolerance too."""
     s = _spec([5, 9, 3], 9, 32, 32, 2, d, dtype, 6)
     print(f"[stages] {dtype} d={d} nq={s.nq}", flush=True)
     q, k, v, do = wl.make_values(s)
@@ -258,11 +260,26 @@ def test_backward_stages_match_the_combined_call(pa, dtype, d):
     mask = pa.build_block_mask(qg, kg)
     o, lse = pa.attn_packed_fwd(Q, K, V, qg, kg, mask, s.scale)
     whole = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask, s.scale)
-    ws = pa.attn_packed_bwd_preprocess(o, DO, lse)
-    dq = pa.attn_packed_bwd_dq(Q, K, V, DO, lse, ws, qg, kg, mask, s.scale)
+    ws = torch.empty(pa.attn_packed_bwd_workspace_bytes(Q.dtype, s.nq, s.nkv, 2, d),
+                     dtype=torch.uint8, device=Q.device)
+    dq = pa.attn_packed_bwd_dq(Q, K, V, o, DO, lse, ws, qg, kg, mask, s.scale)
     dk, dv = pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, qg, kg, mask, s.scale)
     for a, b in zip(whole, (dq, dk, dv)):
         assert torch.equal(a, b)
+    # the row terms the dQ stage leaves in the workspace equal the preprocess's
+    # up to summation order: Delta = rowsum(dO * O) and the LSE in log2 units
+    rows = ws[:2 * 2 * s.nq * 4].view(torch.float32).view(2, 2, s.nq).clone()
+    ws2 = pa.attn_packed_bwd_preprocess(o, DO, lse)
+    pre = ws2[:2 * 2 * s.nq * 4].view(torch.float32).view(2, 2, s.nq)
+    assert torch.equal(torch.isinf(rows[1]), torch.isinf(pre[1]))
+    fin = torch.isfinite(pre[1])
+    assert torch.allclose(rows[1][fin], pre[1][fin], rtol=0, atol=0)
+    assert torch.allclose(rows[0], pre[0], rtol=1e-5, atol=1e-5)
+    dk2, dv2 = pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws2, qg, kg, mask, s.scale)
+    ref0 = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
+    q_ok, k_ok = row_has_pair(qo, ko)
+    compare("dK (preprocess row terms)", host64(dk2), ref0["dk"], k_ok, dtype)
+    compare("dV (preprocess row terms)", host64(dv2), ref0["dv"], k_ok, dtype)
     ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
     got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(dq),
                dk=host64(dk), dv=host64(dv))
@@ -336,11 +353,11 @@ def test_binding_refuses_wrong_output_buffers(pa):
                            workspace=torch.empty(16, dtype=torch.float32, device=dev))
     ws = pa.attn_packed_bwd_preprocess(o, DO, lse)
     with pytest.raises(ValueError):
-        pa.attn_packed_bwd_dq(Q, K, V, DO, lse, ws, qg, kg, mask, dq=torch.empty_like(K))
+        pa.attn_packed_bwd_dq(Q, K, V, o, DO, lse, ws, qg, kg, mask, dq=torch.empty_like(K))
     with pytest.raises(ValueError):
         pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, qg, kg, mask, dk=torch.empty_like(Q))
     with pytest.raises(ValueError):
-        pa.attn_packed_bwd_dq(Q, K, V, DO, lse[:, :-1].contiguous(), ws, qg, kg, mask)
+        pa.attn_packed_bwd_dq(Q, K, V, o, DO, lse[:, :-1].contiguous(), ws, qg, kg, mask)
     with pytest.raises(ValueError):
         pa.attn_packed_bwd_dkdv(Q, K, V, DO, lse, ws, qg, kg[:-1].contiguous(), mask)
     # the checks refused everything above before a launch: the good call still matches
