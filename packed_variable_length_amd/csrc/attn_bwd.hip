@@ -911,14 +911,23 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   // every wave stages 4 of a sub-tile's 32 row groups (2 of Q, 2 of dO): row
   // groups wq + 4 (2 grp + j) of each, piece j in the step's phase j, so the
   // direct loads of a step spread over all eight waves and both phases
-  const auto load_one = [&](int t, int j, int q0, char* stage) __attribute__((always_inline)) {
+  // rsrc[t]: descriptor over the rows of Q (t = 0) or dO (t = 1) from the step's
+  // first query on, built once per step (rebuilding it for every load cost 4 %)
+  const auto load_one = [&](const u32x4_t* rsrc, int t, int j, char* stage)
+                            __attribute__((always_inline)) {
     const int blk = wq + 4 * (2 * grp + j);
-    dma_b128(rows(t ? dout : q, q0), lane_off + blk * group_bytes,
-             lds_address(stage + t * kSpSub + blk * 1024));
+    dma_b128(rsrc[t], lane_off + blk * group_bytes, lds_address(stage + t * kSpSub + blk * 1024));
+  };
+  const auto step_rsrc = [&](int q0, u32x4_t* rsrc) __attribute__((always_inline)) {
+    rsrc[0] = rows(q, q0);
+    rsrc[1] = rows(dout, q0);
+    asm volatile("" ::"s"(rsrc[0]), "s"(rsrc[1]));
   };
   const auto load_piece = [&](int j, int q0, char* stage) __attribute__((always_inline)) {
-    load_one(0, j, q0, stage);
-    load_one(1, j, q0, stage);
+    u32x4_t r[2];
+    step_rsrc(q0, r);
+    load_one(r, 0, j, stage);
+    load_one(r, 1, j, stage);
   };
   // D wave wq stages the ids (0), LSE2 (1) or Delta (2, and again 3) of 64 queries
   // (so each D wave issues 5 loads per step, each P wave 4): the buffer form
@@ -1140,11 +1149,13 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     constexpr int K = decltype(kind)::value;
     xstep = s;
     const int q0 = q0_of(s + 2, qt_l);
+    u32x4_t rs2[2];
+    if (K != 1) step_rsrc(q0, rs2);
     constexpr int nbat = K == 2 ? 8 : 4;
     // dV (dO^T of s - 1), S (Q of s); piece 0 of s + 2 issued between MFMAs
     mfma_phase(kind, prev + kSpSub, cur, [&](int i) __attribute__((always_inline)) {
-      if (K != 1 && i == 1) load_one(0, 0, q0, ld);
-      if (K != 1 && i == nbat - 2) load_one(1, 0, q0, ld);
+      if (K != 1 && i == 1) load_one(rs2, 0, 0, ld);
+      if (K != 1 && i == nbat - 2) load_one(rs2, 1, 0, ld);
     });
     if (K != 1) {
       read_words(cur, kSpLse);
@@ -1153,9 +1164,9 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     fence();
     __builtin_amdgcn_s_setprio(0);
     if (K != 1) prefetch(Mid{}, cur + kSpSub, cur);  // dV of s in step s + 1 (rows not yet used)
-    if (K != 1) load_one(0, 1, q0, ld);
+    if (K != 1) load_one(rs2, 0, 1, ld);
     fetch_next(s);
-    if (K != 1) p_phase([&]() __attribute__((always_inline)) { load_one(1, 1, q0, ld); });
+    if (K != 1) p_phase([&]() __attribute__((always_inline)) { load_one(rs2, 1, 1, ld); });
     pin_ob();
     land_next();
     rotate();
@@ -1170,16 +1181,18 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     constexpr int K = decltype(kind)::value;
     xstep = s;
     const int q0 = q0_of(s + 2, qt_l);
+    u32x4_t rs2[2];
+    if (K != 1) step_rsrc(q0, rs2);
     constexpr int nbat = K == 2 ? 8 : 4;
-    if (K != 1) load_one(0, 0, q0, ld);
+    if (K != 1) load_one(rs2, 0, 0, ld);
     if (K != 0) {
       ds_phase([&]() __attribute__((always_inline)) {
-        if (K != 1) load_one(1, 0, q0, ld);
+        if (K != 1) load_one(rs2, 1, 0, ld);
       });
       pin_ob();    // dS done (and its waits for the P reads) before what follows
       post_xch();  // P of step s - 1 read: the P wave may write that of step s
     } else {
-      load_one(1, 0, q0, ld);
+      load_one(rs2, 1, 0, ld);
     }
     // after the hand-over's LDS accesses, whose waits would otherwise also
     // wait for these scalar loads
@@ -1191,8 +1204,8 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     __builtin_amdgcn_s_setprio(2);
     // dK (Q^T of s - 1), dP (dO of s); piece 1 of s + 2 issued between MFMAs
     mfma_phase(kind, prev, cur + kSpSub, [&](int i) __attribute__((always_inline)) {
-      if (K != 1 && i == 1) load_one(0, 1, q0, ld);
-      if (K != 1 && i == nbat - 2) load_one(1, 1, q0, ld);
+      if (K != 1 && i == 1) load_one(rs2, 0, 1, ld);
+      if (K != 1 && i == nbat - 2) load_one(rs2, 1, 1, ld);
     });
     if (K != 1) read_words(cur, kSpDelta);  // Delta of s, for dS in the next step
     // the scalars land here, after the MFMA phase: their wait (lgkmcnt(0))
