@@ -9,18 +9,21 @@
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
 //   1. tile_summary  one wave per tile of either axis: number of valid tokens and
-//                    up to four distinct valid ids (or "more than four").
-//   2. classify      one thread per tile pair, 32x32 pairs per block: decides the
-//                    class from the two summaries whenever both list all their ids;
-//                    otherwise queues the pair.  Writes the class matrix and its
-//                    transpose (through LDS, so both writes are coalesced).
+//                    up to four distinct valid ids (or "more than four"); also
+//                    clears the row counts.
+//   2. classify      64 x 64 tile pairs per block, the 128 summaries staged in
+//                    LDS: decides the class from the two summaries whenever both
+//                    list all their ids, otherwise queues the pair.  Each thread
+//                    classifies 16 pairs of one row of the class matrix and writes
+//                    them as one 16-byte store, then 16 of its transpose the same
+//                    way, and adds its rows' non-empty counts (one atomic each).
 //   3. resolve       persistent waves settle queued pairs by an exact scan of the
-//                    two tiles' ids (interleaved-id inputs only).
-//   4. count         one block per row of the class matrix and of its transpose.
-//   5. scan_sort     two blocks: exclusive scan of the counts into CSR row
+//                    two tiles' ids (interleaved-id inputs only), and count them.
+//   4. scan_sort     two blocks: exclusive scan of the counts into CSR row
 //                    pointers, and a bitonic sort giving the longest-first order.
-//   6. compact       one block per row: ascending column lists via wave ballots.
-//   7. pair_compact  one block per pair of query tiles (positions 2w, 2w+1 of the
+//   5. compact       one block per row: ascending column lists, 16 classes per
+//                    thread per pass, positions from a block-wide prefix sum.
+//   6. pair_compact  one block per pair of query tiles (positions 2w, 2w+1 of the
 //                    longest-first order, the pairs the paired attention kernels
 //                    run): the ascending union of the two key-tile lists, each
 //                    entry the key tile with both tiles' classes packed beside it,
@@ -29,6 +32,8 @@
 #include "pa_common.h"
 
 namespace {
+
+using pa::u32x4;
 
 constexpr int kMaxTiles = 16384;      // per axis; bounds the sort in LDS
 constexpr int kSortThreads = 1024;
@@ -55,13 +60,15 @@ __global__ void __launch_bounds__(256)
 tile_summary_kernel(const int32_t* __restrict__ q_ids, int32_t nq, int32_t bq, int32_t nqt,
                     const int32_t* __restrict__ kv_ids, int32_t nkv, int32_t bkv, int32_t nkt,
                     TileSummary* __restrict__ q_sum, TileSummary* __restrict__ kv_sum,
-                    int32_t* __restrict__ queue_count) {
+                    int32_t* __restrict__ queue_count, int32_t* __restrict__ cnt_q,
+                    int32_t* __restrict__ cnt_kv) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w == 0 && lane == 0) *queue_count = 0;
   if (w >= nqt + nkt) return;
   const bool qside = w < nqt;
   const int tile = qside ? w : w - nqt;
+  if (lane == 0) (qside ? cnt_q : cnt_kv)[tile] = 0;
   const int32_t* ids = qside ? q_ids : kv_ids;
   const int n = qside ? nq : nkv;
   const int block = qside ? bq : bkv;
@@ -103,50 +110,121 @@ tile_summary_kernel(const int32_t* __restrict__ q_ids, int32_t nq, int32_t bq, i
 }
 
 // ---------------------------------------------------------------- 2. classify
+constexpr int kAmbiguous = -1;
+
+// Class of a tile pair from the two summaries, or kAmbiguous when a tile holds
+// more than four distinct ids (the exact scan of resolve_kernel decides).
+__device__ __forceinline__ int pair_class(const TileSummary& a, const TileSummary& b, int bq,
+                                          int bkv) {
+  if (a.n_valid == 0 || b.n_valid == 0) return 0;
+  if (a.n_ids > 4 || b.n_ids > 4) return kAmbiguous;
+  bool common = false;
+  for (int x = 0; x < a.n_ids; ++x)
+    for (int y = 0; y < b.n_ids; ++y) common |= a.ids[x] == b.ids[y];
+  if (!common) return 0;
+  // full: one id on both sides and every position of both full-length tiles valid
+  return (a.n_ids == 1 && b.n_ids == 1 && a.n_valid == bq && b.n_valid == bkv) ? 2 : 1;
+}
+
+// 16 class bytes to dst[0 .. count) (count <= 16): one 16-byte store when the
+// run is whole and aligned, word stores when word-aligned, else bytes.
+__device__ __forceinline__ void store_classes(uint8_t* dst, const uint32_t (&w)[4], int count) {
+  const uintptr_t a = (uintptr_t)dst;
+  if (count == 16 && (a & 15) == 0) {
+    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+  } else if ((a & 3) == 0) {
+    int k = 0;
+    for (; k + 4 <= count; k += 4) *(uint32_t*)(dst + k) = w[k >> 2];
+    for (; k < count; ++k) dst[k] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+  } else {
+    for (int k = 0; k < count; ++k) dst[k] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+  }
+}
+
+// Block = 64 query tiles x 64 key tiles.  Thread t classifies row t / 4, columns
+// 16 (t % 4) .. + 15 of the class matrix (queueing ambiguous pairs), then column
+// t / 4, rows 16 (t % 4) .. + 15 for the transpose (ambiguous pairs written 0
+// in both, settled by resolve_kernel).  The four threads of a row add their
+// non-empty counts with one atomic.
+// A tile's summary as one code: its id (>= 0) when it holds exactly one id
+// below 2^30 (plus 1 << 30 when every position of a full-length tile carries
+// it), -1 when it holds no valid token, -2 otherwise (pair_class on the full
+// summaries).
+__device__ __forceinline__ int tile_code(const TileSummary& a, int block) {
+  if (a.n_valid == 0) return -1;
+  if (a.n_ids != 1 || a.ids[0] >= (1 << 30)) return -2;
+  return a.ids[0] | (a.n_valid == block ? (1 << 30) : 0);
+}
+
+__device__ __forceinline__ int code_class(int ca, int cb, const TileSummary& a,
+                                          const TileSummary& b, int bq, int bkv) {
+  if ((ca | cb) >= 0) {  // one id on each side
+    if (((ca ^ cb) & ~(1 << 30)) != 0) return 0;
+    return (ca & cb & (1 << 30)) ? 2 : 1;
+  }
+  if (ca == -1 || cb == -1) return 0;
+  return pair_class(a, b, bq, bkv);
+}
+
 __global__ void __launch_bounds__(256)
 classify_kernel(const TileSummary* __restrict__ q_sum, const TileSummary* __restrict__ kv_sum,
                 int32_t nqt, int32_t nkt, int32_t bq, int32_t bkv, uint8_t* __restrict__ cls,
                 uint8_t* __restrict__ cls_t, int32_t* __restrict__ queue,
-                int32_t* __restrict__ queue_count) {
-  __shared__ uint8_t tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int I0 = blockIdx.y * 32, J0 = blockIdx.x * 32;
-  const int J = J0 + tx;
-  for (int r = 0; r < 4; ++r) {
-    const int i = ty + 8 * r;
-    const int I = I0 + i;
-    uint8_t c = 0;
-    if (I < nqt && J < nkt) {
-      const TileSummary a = q_sum[I];
-      const TileSummary b = kv_sum[J];
-      if (a.n_valid == 0 || b.n_valid == 0) {
-        c = 0;
-      } else if (a.n_ids <= 4 && b.n_ids <= 4) {
-        bool common = false;
-        for (int x = 0; x < a.n_ids; ++x)
-          for (int y = 0; y < b.n_ids; ++y) common |= a.ids[x] == b.ids[y];
-        if (!common) {
-          c = 0;
-        } else if (a.n_ids == 1 && b.n_ids == 1 && a.n_valid == bq && b.n_valid == bkv) {
-          c = 2;  // every token of both full-length tiles carries the same id
-        } else {
-          c = 1;
-        }
-      } else {
-        c = 0;  // settled by resolve_kernel
-        const int slot = atomicAdd(queue_count, 1);
-        queue[slot] = I * nkt + J;
-      }
-      cls[(size_t)I * nkt + J] = c;
-    }
-    tile[i][tx] = c;
+                int32_t* __restrict__ queue_count, int32_t* __restrict__ cnt_q,
+                int32_t* __restrict__ cnt_kv) {
+  __shared__ TileSummary sq[64], sk[64];
+  __shared__ int cq[64], ck[64];
+  const int t = threadIdx.x;
+  const int I0 = blockIdx.y * 64, J0 = blockIdx.x * 64;
+  if (t < 64 && I0 + t < nqt) {
+    sq[t] = q_sum[I0 + t];
+    cq[t] = tile_code(sq[t], bq);
+  }
+  if (t >= 64 && t < 128 && J0 + t - 64 < nkt) {
+    sk[t - 64] = kv_sum[J0 + t - 64];
+    ck[t - 64] = tile_code(sk[t - 64], bkv);
   }
   __syncthreads();
-  // transposed write: thread tx now walks the query-tile axis
-  for (int r = 0; r < 4; ++r) {
-    const int j = ty + 8 * r;
-    const int Jt = J0 + j, It = I0 + tx;
-    if (Jt < nkt && It < nqt) cls_t[(size_t)Jt * nqt + It] = tile[tx][j];
+  const int r = t >> 2, c0 = 16 * (t & 3);
+  // rows of the class matrix
+  {
+    const int I = I0 + r;
+    const int cnt = I < nqt ? min(16, nkt - (J0 + c0)) : 0;
+    uint32_t w[4] = {0, 0, 0, 0};
+    int nz = 0;
+    const int ca = cnt > 0 ? cq[r] : 0;
+    for (int k = 0; k < cnt; ++k) {
+      int c = code_class(ca, ck[c0 + k], sq[r], sk[c0 + k], bq, bkv);
+      if (c == kAmbiguous) {
+        const int slot = atomicAdd(queue_count, 1);
+        queue[slot] = I * nkt + J0 + c0 + k;
+        c = 0;
+      }
+      nz += c != 0;
+      w[k >> 2] |= (uint32_t)c << (8 * (k & 3));
+    }
+    if (cnt > 0) store_classes(cls + (size_t)I * nkt + J0 + c0, w, cnt);
+    nz += __shfl_xor(nz, 1, 64);
+    nz += __shfl_xor(nz, 2, 64);
+    if ((t & 3) == 0 && I < nqt && nz) atomicAdd(&cnt_q[I], nz);
+  }
+  // rows of the transpose
+  {
+    const int J = J0 + r;
+    const int cnt = J < nkt ? min(16, nqt - (I0 + c0)) : 0;
+    uint32_t w[4] = {0, 0, 0, 0};
+    int nz = 0;
+    const int cb = cnt > 0 ? ck[r] : 0;
+    for (int k = 0; k < cnt; ++k) {
+      int c = code_class(cq[c0 + k], cb, sq[c0 + k], sk[r], bq, bkv);
+      if (c == kAmbiguous) c = 0;
+      nz += c != 0;
+      w[k >> 2] |= (uint32_t)c << (8 * (k & 3));
+    }
+    if (cnt > 0) store_classes(cls_t + (size_t)J * nqt + I0 + c0, w, cnt);
+    nz += __shfl_xor(nz, 1, 64);
+    nz += __shfl_xor(nz, 2, 64);
+    if ((t & 3) == 0 && J < nkt && nz) atomicAdd(&cnt_kv[J], nz);
   }
 }
 
@@ -159,7 +237,8 @@ resolve_kernel(const int32_t* __restrict__ q_ids, int32_t nq, int32_t bq,
                const int32_t* __restrict__ kv_ids, int32_t nkv, int32_t bkv, int32_t nqt,
                int32_t nkt, const int32_t* __restrict__ queue,
                const int32_t* __restrict__ queue_count, uint8_t* __restrict__ cls,
-               uint8_t* __restrict__ cls_t) {
+               uint8_t* __restrict__ cls_t, int32_t* __restrict__ cnt_q,
+               int32_t* __restrict__ cnt_kv) {
   __shared__ int32_t kbuf[4][1024];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int total_waves = gridDim.x * 4;
@@ -185,33 +264,17 @@ resolve_kernel(const int32_t* __restrict__ q_ids, int32_t nq, int32_t bq,
       const uint8_t c = found ? 1 : 0;
       cls[(size_t)I * nkt + J] = c;
       cls_t[(size_t)J * nqt + I] = c;
+      if (found) {
+        atomicAdd(&cnt_q[I], 1);
+        atomicAdd(&cnt_kv[J], 1);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
-// ---------------------------------------------------------------- 4. count
-__global__ void __launch_bounds__(256)
-count_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_t, int32_t nqt,
-             int32_t nkt, int32_t* __restrict__ cnt_q, int32_t* __restrict__ cnt_kv) {
-  __shared__ int part[4];
-  const int row = blockIdx.x;
-  const bool qside = row < nqt;
-  const uint8_t* src = qside ? cls + (size_t)row * nkt : cls_t + (size_t)(row - nqt) * nqt;
-  const int len = qside ? nkt : nqt;
-  int c = 0;
-  for (int j = threadIdx.x; j < len; j += 256) c += src[j] != 0;
-  c = wave_sum(c);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int t = part[0] + part[1] + part[2] + part[3];
-    if (qside) cnt_q[row] = t; else cnt_kv[row - nqt] = t;
-  }
-}
-
-// ---------------------------------------------------------------- 5. scan + sort
+// ---------------------------------------------------------------- 4. scan + sort
 // Block 0 handles the query side, block 1 the key side.
 __global__ void __launch_bounds__(kSortThreads)
 scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ cnt_kv,
@@ -248,29 +311,31 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   }
   if (t == kSortThreads - 1) ptr[n] = partial[t];
 
-  // longest-first order: sort keys (other - cnt) * n + index ascending
+  // longest-first order: sort keys (other - cnt) << 14 | index ascending (index
+  // < 16384 = kMaxTiles, count <= other <= 16384: 29 bits)
   int P = 1;
   while (P < n) P <<= 1;
   for (int i = t; i < P; i += kSortThreads)
-    keys[i] = i < n ? (uint32_t)(other - cnt[i]) * (uint32_t)n + (uint32_t)i : 0xFFFFFFFFu;
+    keys[i] = i < n ? ((uint32_t)(other - cnt[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
   __syncthreads();
+  // bitonic network; compare-exchange pair p of a stage joins i and i + j,
+  // where i is p with a zero bit inserted at position log2(j)
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = t; i < P; i += kSortThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint32_t a = keys[i], b = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[ixj] = a;
-          }
+      for (int p = t; p < (P >> 1); p += kSortThreads) {
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+        const int ixj = i + j;
+        const uint32_t a = keys[i], b = keys[ixj];
+        const bool up = (i & k) == 0;
+        if ((a > b) == up) {
+          keys[i] = b;
+          keys[ixj] = a;
         }
       }
       __syncthreads();
     }
   }
-  for (int i = t; i < n; i += kSortThreads) order[i] = (int32_t)(keys[i] % (uint32_t)n);
+  for (int i = t; i < n; i += kSortThreads) order[i] = (int32_t)(keys[i] & 0x3FFFu);
   if (!qside) return;
 
   // query side: room for each pair's union list (the sum of its two list
@@ -279,8 +344,8 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   const int pchunk = (np + kSortThreads - 1) / kSortThreads;
   const int p0 = t * pchunk, p1 = min(np, p0 + pchunk);
   const auto cap = [&](int w) {
-    const int a = (int)(keys[2 * w] % (uint32_t)n);
-    return cnt[a] + (2 * w + 1 < n ? cnt[(int)(keys[2 * w + 1] % (uint32_t)n)] : 0);
+    const int a = (int)(keys[2 * w] & 0x3FFFu);
+    return cnt[a] + (2 * w + 1 < n ? cnt[(int)(keys[2 * w + 1] & 0x3FFFu)] : 0);
   };
   int plocal = 0;
   for (int w = p0; w < p1; ++w) plocal += cap(w);
@@ -301,37 +366,72 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   if (t == kSortThreads - 1) pair_off[np] = partial[t];
 }
 
-// ---------------------------------------------------------------- 6. compact
+// ---------------------------------------------------------------- 5. compact
+// Bytes src[j .. j + 16) of a row of `len` bytes as four words (bytes past the
+// row read as 0): one 16-byte load when whole and aligned.
+__device__ __forceinline__ void load_classes(const uint8_t* __restrict__ src, int j, int len,
+                                             uint32_t (&w)[4]) {
+  const uint8_t* p = src + j;
+  if (j + 16 <= len && ((uintptr_t)p & 15) == 0) {
+    const u32x4 v = *(const u32x4*)p;
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    return;
+  }
+  w[0] = w[1] = w[2] = w[3] = 0;
+  for (int k = 0; k < 16 && j + k < len; ++k) w[k >> 2] |= (uint32_t)p[k] << (8 * (k & 3));
+}
+
+__device__ __forceinline__ int class_byte(const uint32_t (&w)[4], int k) {
+  return (int)((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+}
+
+// Exclusive prefix over the block's 256 threads of v (pass total in *total).
+__device__ __forceinline__ int block_exclusive(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int off = incl - v;
+  for (int x = 0; x < wv; ++x) off += wsum[x];
+  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();  // wsum is rewritten by the next pass
+  return off;
+}
+
+// One block per row of the class matrix (key-tile lists) or of its transpose
+// (query-tile lists); thread t takes 16 consecutive tiles per pass.
 __global__ void __launch_bounds__(256)
 compact_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_t, int32_t nqt,
                int32_t nkt, const int32_t* __restrict__ q_ptr,
                const int32_t* __restrict__ kv_ptr, int32_t* __restrict__ q_cols,
                int32_t* __restrict__ kv_rows) {
-  __shared__ int wave_tot[4];
+  __shared__ int wsum[4];
   const int row = blockIdx.x;
   const bool qside = row < nqt;
   const int r = qside ? row : row - nqt;
   const uint8_t* src = qside ? cls + (size_t)r * nkt : cls_t + (size_t)r * nqt;
   const int len = qside ? nkt : nqt;
   int32_t* dst = qside ? q_cols + q_ptr[r] : kv_rows + kv_ptr[r];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   int base = 0;
-  for (int j0 = 0; j0 < len; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    const bool nz = j < len && src[j] != 0;
-    const uint64_t m = __ballot(nz);
-    if (lane == 0) wave_tot[wv] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wv; ++w) off += wave_tot[w];
-    if (nz) dst[off + __popcll(m & lt)] = j;
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    __syncthreads();
+  for (int j0 = 0; j0 < len; j0 += 4096) {
+    const int j = j0 + 16 * threadIdx.x;
+    uint32_t w[4];
+    load_classes(src, j, len, w);
+    int nz = 0;
+    for (int k = 0; k < 16; ++k) nz += class_byte(w, k) != 0;
+    int total;
+    int off = base + block_exclusive(nz, wsum, &total);
+    for (int k = 0; k < 16; ++k)
+      if (class_byte(w, k) != 0) dst[off++] = j + k;
+    base += total;
   }
 }
 
-// ---------------------------------------------------------------- 7. pair lists
+// ---------------------------------------------------------------- 6. pair lists
 // Block w: query tiles a = q_order[2w] and b = q_order[2w + 1] (none past the
 // end).  Entry = key tile | class(a, kt) << 16 | class(b, kt) << 24 for every
 // key tile at least one of the two rows has an allowed pair with, ascending.
@@ -339,29 +439,28 @@ __global__ void __launch_bounds__(256)
 pair_compact_kernel(const uint8_t* __restrict__ cls, int32_t nqt, int32_t nkt,
                     const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
                     int32_t* __restrict__ pair_len, int32_t* __restrict__ pair_ent) {
-  __shared__ int wave_tot[4];
+  __shared__ int wsum[4];
   const int w = blockIdx.x;
   const int a = q_order[2 * w];
   const int b = 2 * w + 1 < nqt ? q_order[2 * w + 1] : -1;
   const uint8_t* ra = cls + (size_t)a * nkt;
   const uint8_t* rb = b >= 0 ? cls + (size_t)b * nkt : nullptr;
   int32_t* dst = pair_ent + pair_off[w];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   int base = 0;
-  for (int j0 = 0; j0 < nkt; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    const int ca = j < nkt ? ra[j] : 0;
-    const int cb = (j < nkt && rb) ? rb[j] : 0;
-    const bool nz = (ca | cb) != 0;
-    const uint64_t m = __ballot(nz);
-    if (lane == 0) wave_tot[wv] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int x = 0; x < wv; ++x) off += wave_tot[x];
-    if (nz) dst[off + __popcll(m & lt)] = j | (ca << 16) | (cb << 24);
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    __syncthreads();
+  for (int j0 = 0; j0 < nkt; j0 += 4096) {
+    const int j = j0 + 16 * threadIdx.x;
+    uint32_t wa[4], wb[4] = {0, 0, 0, 0};
+    load_classes(ra, j, nkt, wa);
+    if (rb) load_classes(rb, j, nkt, wb);
+    int nz = 0;
+    for (int k = 0; k < 16; ++k) nz += (class_byte(wa, k) | class_byte(wb, k)) != 0;
+    int total;
+    int off = base + block_exclusive(nz, wsum, &total);
+    for (int k = 0; k < 16; ++k) {
+      const int ca = class_byte(wa, k), cb = class_byte(wb, k);
+      if (ca | cb) dst[off++] = (j + k) | (ca << 16) | (cb << 24);
+    }
+    base += total;
   }
   if (threadIdx.x == 0) pair_len[w] = base;
 }
@@ -448,14 +547,15 @@ extern "C" int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const i
 
   const int waves = nqt + nkt;
   hipLaunchKernelGGL(tile_summary_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, q_seq_id, nq,
-                     block_q, nqt, kv_seq_id, nkv, block_kv, nkt, q_sum, kv_sum, queue_count);
-  hipLaunchKernelGGL(classify_kernel, dim3((nkt + 31) / 32, (nqt + 31) / 32), dim3(256), 0, s,
-                     q_sum, kv_sum, nqt, nkt, block_q, block_kv, cls, cls_t, queue, queue_count);
+                     block_q, nqt, kv_seq_id, nkv, block_kv, nkt, q_sum, kv_sum, queue_count,
+                     cnt_q, cnt_kv);
+  hipLaunchKernelGGL(classify_kernel, dim3((nkt + 63) / 64, (nqt + 63) / 64), dim3(256), 0, s,
+                     q_sum, kv_sum, nqt, nkt, block_q, block_kv, cls, cls_t, queue, queue_count,
+                     cnt_q, cnt_kv);
   const size_t pairs = (size_t)nqt * nkt;
   const int rblocks = (int)std::min<size_t>((pairs + 3) / 4, 1024);
   hipLaunchKernelGGL(resolve_kernel, dim3(rblocks), dim3(256), 0, s, q_seq_id, nq, block_q,
-                     kv_seq_id, nkv, block_kv, nqt, nkt, queue, queue_count, cls, cls_t);
-  hipLaunchKernelGGL(count_kernel, dim3(nqt + nkt), dim3(256), 0, s, cls, cls_t, nqt, nkt, cnt_q,
+                     kv_seq_id, nkv, block_kv, nqt, nkt, queue, queue_count, cls, cls_t, cnt_q,
                      cnt_kv);
   hipLaunchKernelGGL(scan_sort_kernel, dim3(2), dim3(kSortThreads), 0, s, cnt_q, cnt_kv, nqt, nkt,
                      q_ptr, kv_ptr, q_order, kv_order, pair_off);

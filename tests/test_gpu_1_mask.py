@@ -107,6 +107,18 @@ def test_mask_interleaved_and_ragged(pa, seed):
         _check_mask(pa, qid, kid, bq, bkv)
 
 
+def test_mask_large_ids(pa):
+    # ids at and above 2^30 (and near the int32 maximum) classify like any other
+    rng = np.random.default_rng(11)
+    base = np.array([0, 5, (1 << 30) - 1, 1 << 30, (1 << 30) + 7, (1 << 31) - 2], np.int64)
+    qid = np.repeat(base, 300).astype(np.int32)
+    kid = np.repeat(base[::-1], 260).astype(np.int32)
+    qid[rng.random(len(qid)) < 0.05] = -1
+    for bq, bkv in ((128, 128), (64, 128), (256, 32)):
+        _check_mask(pa, qid, kid, bq, bkv)
+        _check_mask(pa, qid, qid, bq, bkv)
+
+
 def test_mask_stress_1m_tokens(pa):
     # 1,048,576 tokens in 4096-token segments, with 2% padding tokens
     n = 1 << 20
