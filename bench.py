@@ -508,11 +508,15 @@ def run_configs(pa, configs, extras_out):
                                          "bucketed sweep, cross (6 action -> 32 video tok/frame)")
         elif c == "5":
             out[c] = r = bench_pack_list(pa, [wl.config(5)], "long-64k (ids given)")
+        elif c == "mask":
+            continue  # the block-mask builder alone, below
         else:
             raise SystemExit(f"unknown config {c}")
         log(f"[bench] config {c}: {r['ms']:.3f} ms, {r['useful_TFLOPs']} TFLOP/s useful "
             f"({100 * r['frac_of_bf16_peak']:.1f}% of bf16 peak)")
     extras_out["configs"] = out
+    if "mask" not in configs:
+        return
     mb = {}
     s3 = wl.config(3)
     vf = torch.from_numpy(s3.valid_frames).to(dev)
@@ -538,8 +542,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=str, default="all",
                     help="heads the oracle baseline computes ('all' or a list like 0,23)")
-    ap.add_argument("--configs", type=str, default="2,4self,4cross,5",
-                    help="other workloads measured after the timed steps ('' for none)")
+    ap.add_argument("--configs", type=str, default="2,4self,4cross,5,mask",
+                    help="other workloads measured after the timed steps ('' for none; "
+                         "'mask' = the block-mask builder alone)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the loss / unpadded-pack / planner / AdaLN measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
