@@ -13,8 +13,9 @@ per head (value_12dPH: the same time counted without the recompute).
 Per-stage times (HIP events on the stream the library launches on) go to
 stderr and into the JSON's "stages_ms" object.  After the timed steps the
 other workloads are measured the same way (extras.configs: the 4 x 120-frame
-pack, all 40 batches of the length-bucketed sweep, self and cross, and the
-64k mixed pack), the block-mask builder alone (extras.mask_builder: GB/s of
+pack, all 40 batches of the length-bucketed sweep, self and cross, the
+64k mixed pack, and the 4 x 288 pack's segments permuted in 512-token pieces),
+the block-mask builder alone (extras.mask_builder: GB/s of
 its algorithmic bytes on the 4 x 288 and 64k packs and a 1,048,576-token case),
 then the next rows (masked loss, unpadded pack, planner, AdaLN) and the fp64
 CPU oracle on all heads of the pack (cpu_baseline).
@@ -508,6 +509,12 @@ def run_configs(pa, configs, extras_out):
                                          "bucketed sweep, cross (6 action -> 32 video tok/frame)")
         elif c == "5":
             out[c] = r = bench_pack_list(pa, [wl.config(5)], "long-64k (ids given)")
+        elif c == "3":
+            out[c] = r = bench_pack_list(pa, [wl.config(3)], "var-4x288 (values drawn on the "
+                                         "device like the other configs)")
+        elif c == "scatter":
+            out[c] = r = bench_pack_list(pa, [wl.scattered_pack()],
+                                         "var-4x288 in permuted 512-token pieces (ids given)")
         elif c == "mask":
             continue  # the block-mask builder alone, below
         else:
@@ -542,7 +549,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=str, default="all",
                     help="heads the oracle baseline computes ('all' or a list like 0,23)")
-    ap.add_argument("--configs", type=str, default="2,4self,4cross,5,mask",
+    ap.add_argument("--configs", type=str, default="2,3,4self,4cross,5,scatter,mask",
                     help="other workloads measured after the timed steps ('' for none; "
                          "'mask' = the block-mask builder alone)")
     ap.add_argument("--no-extras", action="store_true",

@@ -172,6 +172,38 @@ def test_bf16_boundary_lengths(pa, cross, d):
     _check(got, ref, qo, ko, "bf16")
 
 
+def test_bf16_score_jump_late_in_the_walk(pa):
+    """Keys deep in the walk whose scores exceed every earlier score of a row by
+    far more than the fp32 range of exp2 (k = 60 q of that row, about 245 in
+    log2 units), and a large negative score: O, LSE and dV still match the
+    oracle, dQ and dK are finite.  The forward raises a row's running max only
+    when a score passes it by more than its lazy threshold, and then rescales
+    O and the row sum; a forward that missed that rescale would return inf or
+    NaN here.  (dQ and dK of a row whose softmax is one-hot
+    come from dP - Delta, a difference of two nearly equal terms of which
+    Delta uses the bf16-rounded O, so their relative error there is that of
+    bf16 rounding, not of the kernels.)"""
+    n, H, d = 900, 2, 128
+    ids = np.zeros(n, np.int32)
+    ids[850:] = 1
+    s = wl.PackSpec("jump", heads=H, head_dim=d, dtype="bf16", seed=77, value_std=0.5,
+                    segment_ids=ids)
+    q, k, v, do = wl.make_values(s)
+    k = k.copy()
+    for h in range(H):
+        k[700, h] = wl.round_to_bf16(60.0 * q[5, h])        # query 5 (tile 0) meets key 700 (tile 5)
+        k[300, h] = wl.round_to_bf16(40.0 * q[140 + h, h])  # queries of tile 1, key of tile 2
+    k[640, 1] = wl.round_to_bf16(-30.0 * q[200, 1])
+    got = _run_gpu(pa, q, k, v, do, ids_dev(ids), ids_dev(ids), "bf16", s.scale)
+    ref = oatt.forward_backward(q, k, v, do, ids, ids, s.scale)
+    assert ref["lse"][0, 5] > 100.0                          # the jump is real
+    q_ok, k_ok = row_has_pair(ids, ids)
+    compare("O", got["o"], ref["o"], q_ok, "bf16")
+    compare("dV", got["dv"], ref["dv"], k_ok, "bf16")
+    compare_lse(got["lse"], ref["lse"])
+    assert np.isfinite(got["dq"]).all() and np.isfinite(got["dk"]).all()
+
+
 def test_bf16_all_padding_pack(pa):
     s = _spec([0, 0], 4, 32, 32, 2, 128, "bf16", 3)
     q, k, v, do = wl.make_values(s)

@@ -5,7 +5,7 @@ Every head of every output is checked on the device: values finite, rows with
 no allowed pair exactly zero, the LSE -inf pattern exactly that of the rows
 without an allowed key.  Values are compared with the fp64 oracle head by head:
 all 24 heads of the 4 x 288-frame and 4 x 120-frame packs, four heads of the
-64k mixed pack, and one head per batch of all 40 batches of the length-bucketed
+64k mixed pack and of the 4 x 288 pack scattered in 512-token pieces, and one head per batch of all 40 batches of the length-bucketed
 sweep, self- and cross-attention (the head rotates over the batches, so every
 head is compared somewhere).  Outputs sit inside guard bands.  Tolerances: see
 tests/_helpers.py.
@@ -111,6 +111,12 @@ def test_equal_4x120_all_heads(pa):
 
 def test_long_mixed_64k(pa):
     _full(pa, wl.config(5), [0, 7, 11, 23])
+
+
+def test_scattered_4x288(pa):
+    """The 4 x 288 pack's segments cut into 512-token pieces and permuted: every
+    tile's key list spans the sequence (the walk visits listed tiles only)."""
+    _full(pa, wl.scattered_pack(), [0, 9, 17, 23])
 
 
 @pytest.fixture(scope="module")

@@ -43,6 +43,20 @@ def test_long_mixed_pack():
     assert (ids[-135:] == -1).all() and (ids[:-135] >= 0).all()
 
 
+def test_scattered_pack():
+    """Same token count per segment as the frame-padded 4 x 288 pack, reordered in
+    512-token pieces: the segments are no longer contiguous."""
+    s = wl.scattered_pack()
+    ids = s.segment_ids
+    assert s.nq == s.nkv == 36864 and (s.heads, s.head_dim) == (24, 128)
+    assert np.bincount(ids[ids >= 0]).tolist() == [3808, 5664, 9120, 7648]
+    assert int((ids < 0).sum()) == 36864 - 26240
+    runs = 1 + int((ids[1:] != ids[:-1]).sum())
+    assert runs > 40                      # scattered: many runs instead of 4 + padding
+    pieces = ids.reshape(72, 512)
+    assert sorted(map(bytes, pieces)) != [bytes(p) for p in pieces]  # reordered
+
+
 def test_round_to_bf16_matches_torch():
     rng = np.random.default_rng(0)
     x = np.concatenate([rng.standard_normal(100000).astype(np.float32),

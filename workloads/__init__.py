@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for packed segment-id attention.
 
 This package only draws inputs: episode lengths, padded frame counts, per-token
-segment ids given directly (long mixed-modality pack), episode token counts
+segment ids given directly (long mixed-modality pack, scattered pack), episode token counts
 of unpadded packs, the random q, k, v, dO values, the random predictions /
 targets of the masked loss and the AdaLN activations and modulation tables.  It holds none of the attention arithmetic and none
 of the seq-id, packing or block-mask construction, so both the CPU oracle and
@@ -20,4 +20,5 @@ from .packs import (  # noqa: F401
     UNPADDED_BUDGET,
     episode_stream,
     unpadded_pack,
+    scattered_pack,
 )

@@ -33,6 +33,7 @@ __all__ = [
     "UNPADDED_BUDGET",
     "episode_stream",
     "unpadded_pack",
+    "scattered_pack",
 ]
 
 
@@ -257,6 +258,27 @@ def unpadded_pack(token_lengths, name: str = "unpadded-68k", budget: int = UNPAD
     return PackSpec(name, heads=heads, head_dim=head_dim, dtype="bf16", seed=seed,
                     value_std=0.5, token_lengths=np.asarray(token_lengths, np.int32),
                     n_tokens=int(budget), notes="episodes back to back, no frame padding")
+
+
+def scattered_pack(chunk: int = 512, seed: int = 0) -> PackSpec:
+    """The 4 x 288-frame pack's token counts in scattered order (segment ids given).
+
+    Four segments of 119, 177, 285 and 239 frames x 32 tokens laid end to end,
+    then padding (-1) up to the same 36,864 tokens; the sequence is cut into
+    ``chunk``-token pieces that a seeded permutation reorders.  Every segment
+    keeps its token count, so the allowed pairs (and the useful work) equal
+    those of the frame-padded pack, while every query tile's key list is
+    spread over the whole sequence (ids need not be sorted or contiguous).
+    """
+    lengths = np.array([119, 177, 285, 239], np.int64) * 32
+    total = 4 * 288 * 32
+    ids = np.full(total, -1, dtype=np.int32)
+    ids[:lengths.sum()] = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+    pieces = ids.reshape(total // chunk, chunk)
+    order = np.random.default_rng(seed).permutation(len(pieces))
+    return PackSpec(f"var-4x288-scattered-{chunk}", heads=24, head_dim=128, dtype="bf16",
+                    seed=7, value_std=0.5, segment_ids=np.ascontiguousarray(pieces[order]).ravel(),
+                    notes=f"4x288 token counts, {chunk}-token pieces permuted")
 
 
 CONFIG_NAMES = ("tiny-f32", "equal-4x120", "var-4x288", "bucketed", "long-64k")
