@@ -97,7 +97,11 @@ struct Row8;
 template <>
 struct Row8<uint16_t> {  // 8 bf16 values = 4 dwords
   u32x4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *(const u32x4*)p; }
+  // rows are read once: non-temporal (streaming) loads and stores
+  // (forward 86 -> 82 us, backward 139 -> 133 us on 36,864 x 3072)
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    r = __builtin_nontemporal_load((const u32x4*)p);
+  }
   // opaque to the optimizer: values derived from r are recomputed after this
   __device__ __forceinline__ void launder() { asm volatile("" : "+v"(r)); }
   __device__ __forceinline__ float at(int j) const {
@@ -120,7 +124,7 @@ __device__ __forceinline__ void store8(uint16_t* p, const float* f) {
   u32x4 a;
 #pragma unroll
   for (int w = 0; w < 4; ++w) a[w] = pack_bf16x2(f[2 * w], f[2 * w + 1]);
-  *(u32x4*)p = a;
+  __builtin_nontemporal_store(a, (u32x4*)p);
 }
 __device__ __forceinline__ void store8(float* p, const float* f) {
   *(f32x4*)p = f32x4{f[0], f[1], f[2], f[3]};
