@@ -310,6 +310,17 @@ int32_t attn_packed_bwd_noalloc(int32_t dtype, int32_t nq, int32_t nkv, int32_t 
 int32_t pa_test_set_handover_spin_limit(int32_t limit);
 
 /*
+ * pa_handover_failures -- how many dK/dV waves on the current device ran out
+ * of their bounded hand-over wait (see above) since the library was loaded or
+ * the count was last reset; each such wave wrote NaN into its dv rows.  For
+ * monitoring a training job: a nonzero count means the gradients of those
+ * launches are not to be used.  Synchronous (a device-to-host copy on the null
+ * stream, so it waits for the device's earlier work); reset != 0 sets the
+ * count back to 0 after reading it.  Returns the count (>= 0), or PA_ERR_HIP.
+ */
+int32_t pa_handover_failures(int32_t reset);
+
+/*
  * Frame-valid masked squared-error loss ("LingBot-VA packing" report, section
  * 2.1, compute_loss: on a padded pack the latent and action losses are averaged
  * over valid frames only).  A token is valid iff its seq id is >= 0:

@@ -31,6 +31,7 @@ from .packattn import (  # noqa: F401
     masked_mse_workspace_bytes,
     pa_status_str,
     pa_test_set_handover_spin_limit,
+    pa_handover_failures,
     plan_token_packs,
     seq_ids_from_lengths,
     seq_ids_from_valid_frames,

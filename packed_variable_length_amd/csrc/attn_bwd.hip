@@ -816,6 +816,11 @@ constexpr int kSpSub = 64 * kRowBytes;                // one 64-query tile (16 K
 constexpr int kSpStage = 2 * kSpSub + 3 * 256;        // Q, dO, ids, LSE2, Delta
 constexpr int kSpIds = 2 * kSpSub, kSpLse = kSpIds + 256, kSpDelta = kSpLse + 256;
 
+// Number of dK/dV waves whose hand-over wait ran out (their dv rows are NaN),
+// since the library was loaded or the count was last reset; one per device.
+// Incremented with a vector atomic by lane 0 of such a wave.
+__device__ int32_t g_handover_failures = 0;
+
 template <int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -1260,6 +1265,8 @@ dkdv_bf16_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
       step_d(n, Last{}, st0, slast, st2);
     }
   }
+  if (xfail && lane == 0)
+    __hip_atomic_fetch_add(&g_handover_failures, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (kin) {
     uint16_t* gp = (grp == 0 ? dv : dk) + (size_t)krow * rs + hoff;
     const float f = grp == 0 ? 1.f : scale;
@@ -1662,6 +1669,20 @@ extern "C" int32_t attn_packed_bwd_noalloc(int32_t dtype, int32_t nq, int32_t nk
     if (st != PA_OK) return st;
   }
   return PA_OK;
+}
+
+extern "C" int32_t pa_handover_failures(int32_t reset) {
+  int32_t n = 0;
+  if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_handover_failures), sizeof(n), 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return PA_ERR_HIP;
+  if (reset) {
+    const int32_t zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_handover_failures), &zero, sizeof(zero), 0,
+                          hipMemcpyHostToDevice) != hipSuccess)
+      return PA_ERR_HIP;
+  }
+  return n;
 }
 
 extern "C" int32_t pa_test_set_handover_spin_limit(int32_t limit) {

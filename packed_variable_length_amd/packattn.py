@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "masked_mse_bwd": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
         "masked_mse_fwd_bwd": (i32, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
         "pa_test_set_handover_spin_limit": (i32, [i32]),
+        "pa_handover_failures": (i32, [i32]),
         "attn_packed_bwd_noalloc_max_bytes": (sz, []),
         "attn_packed_bwd_noalloc": (i32, [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                           vp, vp, pm, vp, vp, vp, vp]),
@@ -116,6 +117,15 @@ def pa_test_set_handover_spin_limit(limit: int) -> int:
     """Test hook: bound of the dK/dV kernel's P hand-over wait for later launches
     (a negative limit restores the default); returns the previous bound."""
     return int(_lib.pa_test_set_handover_spin_limit(int(limit)))
+
+
+def pa_handover_failures(reset: bool = False) -> int:
+    """Count of dK/dV waves whose P hand-over wait ran out (their dv rows are
+    NaN) on the current device since load or the last reset; synchronous."""
+    n = int(_lib.pa_handover_failures(1 if reset else 0))
+    if n < 0:
+        raise PackAttnError(n, "pa_handover_failures")
+    return n
 
 
 def _check(status: int, where: str) -> None:

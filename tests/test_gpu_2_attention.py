@@ -324,7 +324,9 @@ def test_handover_wait_that_runs_out_poisons_dv(pa):
     (a bound of zero polls), the waiting waves write NaN into their dv rows
     instead of values -- every key tile with work has such a wait -- and the
     kernel still ends normally; back at the default bound the results match
-    the oracle again."""
+    the oracle again.  The device-side count of such waves
+    (pa_handover_failures) is nonzero after the forced run and zero after the
+    normal one."""
     s = _spec([5, 9, 3], 9, 32, 32, 2, 128, "bf16", 4)
     q, k, v, do = wl.make_values(s)
     (qo, ko), (qg, kg) = _ids_from_spec(pa, s)
@@ -335,6 +337,7 @@ def test_handover_wait_that_runs_out_poisons_dv(pa):
     tile_has_work = np.array([(ko[128 * t:128 * (t + 1)] >= 0).any() for t in range(ntiles)])
     rows_with_work = np.repeat(tile_has_work, 128)[: s.nkv]
     assert tile_has_work.any() and not tile_has_work.all()
+    pa.pa_handover_failures(reset=True)
     default = pa.pa_test_set_handover_spin_limit(0)
     try:
         assert default == 1 << 20
@@ -345,7 +348,10 @@ def test_handover_wait_that_runs_out_poisons_dv(pa):
         assert pa.pa_test_set_handover_spin_limit(-1) == 0
     assert np.isnan(dv[rows_with_work]).all()
     assert (dv[~rows_with_work] == 0).all()
+    assert pa.pa_handover_failures(reset=True) > 0
     g = pa.attn_packed_bwd(Q, K, V, o, DO, lse, qg, kg, mask)
+    torch.cuda.synchronize()
+    assert pa.pa_handover_failures() == 0
     ref = oatt.forward_backward(q, k, v, do, qo, ko, s.scale)
     got = dict(o=host64(o), lse=lse.cpu().numpy().astype(np.float64), dq=host64(g[0]),
                dk=host64(g[1]), dv=host64(g[2]))
