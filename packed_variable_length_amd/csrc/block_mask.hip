@@ -20,10 +20,13 @@
 //   3. resolve       persistent waves settle queued pairs by an exact scan of the
 //                    two tiles' ids (interleaved-id inputs only), and count them.
 //   4. scan_sort     two blocks: exclusive scan of the counts into CSR row
-//                    pointers, and a bitonic sort giving the longest-first order.
-//   5. compact       one block per row: ascending column lists, 16 classes per
-//                    thread per pass, positions from a block-wide prefix sum.
-//   6. pair_compact  one block per pair of query tiles (positions 2w, 2w+1 of the
+//                    pointers (shuffle scans per wave), and a bitonic sort giving
+//                    the longest-first order (partner distances below 128 in
+//                    registers, the rest through LDS).
+//   5. lists         one launch, two kinds of block.  One block per row:
+//                    ascending column lists, 16 classes per thread per pass,
+//                    positions from a block-wide prefix sum.  One block per
+//                    pair of query tiles (positions 2w, 2w+1 of the
 //                    longest-first order, the pairs the paired attention kernels
 //                    run): the ascending union of the two key-tile lists, each
 //                    entry the key tile with both tiles' classes packed beside it,
@@ -275,6 +278,102 @@ resolve_kernel(const int32_t* __restrict__ q_ids, int32_t nq, int32_t bq,
 }
 
 // ---------------------------------------------------------------- 4. scan + sort
+// Exclusive prefix of v over the kSortThreads threads (total in *total): a
+// shuffle scan inside each wave, then the wave totals (two barriers).
+constexpr int kSortWaves = kSortThreads / 64;
+__device__ __forceinline__ int sort_block_exclusive(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int off = incl - v, tot = 0;
+  for (int x = 0; x < kSortWaves; ++x) {
+    const int w = wsum[x];
+    off += x < wv ? w : 0;
+    tot += w;
+  }
+  *total = tot;
+  __syncthreads();  // wsum is rewritten by the next scan
+  return off;
+}
+
+// Compare-exchange of a bitonic stage (block size k, partner distance j) on the
+// element at position pos holding a, whose partner holds b: the lower element
+// of an ascending pair keeps the minimum.
+__device__ __forceinline__ uint32_t bitonic_keep(uint32_t a, uint32_t b, int pos, int j, int k) {
+  const bool lower = (pos & j) == 0, up = (pos & k) == 0;
+  return lower == up ? min(a, b) : max(a, b);
+}
+
+// Ascending bitonic sort of keys[0 .. P) in LDS, P a power of two.  Stages
+// whose partner distance j is >= 128 exchange through LDS (one barrier each);
+// the rest run in registers: a wave holds a 128-key block, lane l the keys at
+// l and l + 64 (so j = 64 pairs a lane's two keys and j < 64 is a shuffle).
+__device__ void bitonic_sort(uint32_t* keys, int P) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int nblk = P >= 128 ? P / 128 : 0;
+  // in-register stages for the block sizes kfirst .. klast (powers of two),
+  // each with its distances min(k / 2, 64) .. 1
+  const auto reg_stages = [&](int kfirst, int klast) {
+    for (int b = wv; b < nblk; b += kSortWaves) {
+      const int base = b * 128;
+      uint32_t e0 = keys[base + lane], e1 = keys[base + 64 + lane];
+      for (int kb = kfirst; kb <= klast; kb <<= 1) {
+        for (int j = min(kb >> 1, 64); j > 0; j >>= 1) {
+          if (j == 64) {
+            const bool up = ((base + lane) & kb) == 0;
+            const uint32_t lo = min(e0, e1), hi = max(e0, e1);
+            e0 = up ? lo : hi;
+            e1 = up ? hi : lo;
+          } else {
+            const uint32_t p0 = (uint32_t)__shfl_xor((int)e0, j, 64);
+            const uint32_t p1 = (uint32_t)__shfl_xor((int)e1, j, 64);
+            e0 = bitonic_keep(e0, p0, base + lane, j, kb);
+            e1 = bitonic_keep(e1, p1, base + 64 + lane, j, kb);
+          }
+        }
+      }
+      keys[base + lane] = e0;
+      keys[base + 64 + lane] = e1;
+    }
+    __syncthreads();
+  };
+  if (P < 128) {  // small: the plain network through LDS
+    for (int k = 2; k <= P; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int p = t; p < (P >> 1); p += kSortThreads) {
+          const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+          const uint32_t a = keys[i], b = keys[i + j];
+          if ((a > b) == ((i & k) == 0)) {
+            keys[i] = b;
+            keys[i + j] = a;
+          }
+        }
+        __syncthreads();
+      }
+    return;
+  }
+  reg_stages(2, 128);  // block sizes 2 .. 128, all in registers
+  for (int k = 256; k <= P; k <<= 1) {
+    for (int j = k >> 1; j >= 128; j >>= 1) {
+      for (int p = t; p < (P >> 1); p += kSortThreads) {
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+        const uint32_t a = keys[i], b = keys[i + j];
+        if ((a > b) == ((i & k) == 0)) {
+          keys[i] = b;
+          keys[i + j] = a;
+        }
+      }
+      __syncthreads();
+    }
+    reg_stages(k, k);
+  }
+}
+
 // Block 0 handles the query side, block 1 the key side.
 __global__ void __launch_bounds__(kSortThreads)
 scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ cnt_kv,
@@ -282,7 +381,7 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
                  int32_t* __restrict__ kv_ptr, int32_t* __restrict__ q_order,
                  int32_t* __restrict__ kv_order, int32_t* __restrict__ pair_off) {
   __shared__ uint32_t keys[kMaxTiles];
-  __shared__ int32_t partial[kSortThreads];
+  __shared__ int wsum[kSortWaves];
   const bool qside = blockIdx.x == 0;
   const int32_t* cnt = qside ? cnt_q : cnt_kv;
   const int n = qside ? nqt : nkt;
@@ -291,25 +390,18 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   int32_t* order = qside ? q_order : kv_order;
   const int t = threadIdx.x;
 
-  // exclusive scan: each thread owns a contiguous chunk
+  // exclusive scan of the counts: each thread owns a contiguous chunk
   const int chunk = (n + kSortThreads - 1) / kSortThreads;
   const int b0 = t * chunk, b1 = min(n, b0 + chunk);
   int local = 0;
   for (int i = b0; i < b1; ++i) local += cnt[i];
-  partial[t] = local;
-  __syncthreads();
-  for (int o = 1; o < kSortThreads; o <<= 1) {  // Hillis-Steele inclusive scan
-    const int v = t >= o ? partial[t - o] : 0;
-    __syncthreads();
-    partial[t] += v;
-    __syncthreads();
-  }
-  int run = partial[t] - local;
+  int total;
+  int run = sort_block_exclusive(local, wsum, &total);
   for (int i = b0; i < b1; ++i) {
     ptr[i] = run;
     run += cnt[i];
   }
-  if (t == kSortThreads - 1) ptr[n] = partial[t];
+  if (t == 0) ptr[n] = total;
 
   // longest-first order: sort keys (other - cnt) << 14 | index ascending (index
   // < 16384 = kMaxTiles, count <= other <= 16384: 29 bits)
@@ -318,23 +410,7 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   for (int i = t; i < P; i += kSortThreads)
     keys[i] = i < n ? ((uint32_t)(other - cnt[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
   __syncthreads();
-  // bitonic network; compare-exchange pair p of a stage joins i and i + j,
-  // where i is p with a zero bit inserted at position log2(j)
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int p = t; p < (P >> 1); p += kSortThreads) {
-        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
-        const int ixj = i + j;
-        const uint32_t a = keys[i], b = keys[ixj];
-        const bool up = (i & k) == 0;
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[ixj] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  bitonic_sort(keys, P);
   for (int i = t; i < n; i += kSortThreads) order[i] = (int32_t)(keys[i] & 0x3FFFu);
   if (!qside) return;
 
@@ -349,21 +425,13 @@ scan_sort_kernel(const int32_t* __restrict__ cnt_q, const int32_t* __restrict__ 
   };
   int plocal = 0;
   for (int w = p0; w < p1; ++w) plocal += cap(w);
-  __syncthreads();
-  partial[t] = plocal;
-  __syncthreads();
-  for (int o = 1; o < kSortThreads; o <<= 1) {
-    const int v = t >= o ? partial[t - o] : 0;
-    __syncthreads();
-    partial[t] += v;
-    __syncthreads();
-  }
-  int prun = partial[t] - plocal;
+  int ptotal;
+  int prun = sort_block_exclusive(plocal, wsum, &ptotal);
   for (int w = p0; w < p1; ++w) {
     pair_off[w] = prun;
     prun += cap(w);
   }
-  if (t == kSortThreads - 1) pair_off[np] = partial[t];
+  if (t == 0) pair_off[np] = ptotal;
 }
 
 // ---------------------------------------------------------------- 5. compact
@@ -404,13 +472,12 @@ __device__ __forceinline__ int block_exclusive(int v, int* wsum, int* total) {
 
 // One block per row of the class matrix (key-tile lists) or of its transpose
 // (query-tile lists); thread t takes 16 consecutive tiles per pass.
-__global__ void __launch_bounds__(256)
-compact_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_t, int32_t nqt,
-               int32_t nkt, const int32_t* __restrict__ q_ptr,
-               const int32_t* __restrict__ kv_ptr, int32_t* __restrict__ q_cols,
-               int32_t* __restrict__ kv_rows) {
-  __shared__ int wsum[4];
-  const int row = blockIdx.x;
+__device__ __forceinline__ void compact_row(const uint8_t* __restrict__ cls,
+                                            const uint8_t* __restrict__ cls_t, int32_t nqt,
+                                            int32_t nkt, const int32_t* __restrict__ q_ptr,
+                                            const int32_t* __restrict__ kv_ptr,
+                                            int32_t* __restrict__ q_cols,
+                                            int32_t* __restrict__ kv_rows, int row, int* wsum) {
   const bool qside = row < nqt;
   const int r = qside ? row : row - nqt;
   const uint8_t* src = qside ? cls + (size_t)r * nkt : cls_t + (size_t)r * nqt;
@@ -435,12 +502,11 @@ compact_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_
 // Block w: query tiles a = q_order[2w] and b = q_order[2w + 1] (none past the
 // end).  Entry = key tile | class(a, kt) << 16 | class(b, kt) << 24 for every
 // key tile at least one of the two rows has an allowed pair with, ascending.
-__global__ void __launch_bounds__(256)
-pair_compact_kernel(const uint8_t* __restrict__ cls, int32_t nqt, int32_t nkt,
-                    const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
-                    int32_t* __restrict__ pair_len, int32_t* __restrict__ pair_ent) {
-  __shared__ int wsum[4];
-  const int w = blockIdx.x;
+__device__ __forceinline__ void pair_row(const uint8_t* __restrict__ cls, int32_t nqt, int32_t nkt,
+                                         const int32_t* __restrict__ q_order,
+                                         const int32_t* __restrict__ pair_off,
+                                         int32_t* __restrict__ pair_len,
+                                         int32_t* __restrict__ pair_ent, int w, int* wsum) {
   const int a = q_order[2 * w];
   const int b = 2 * w + 1 < nqt ? q_order[2 * w + 1] : -1;
   const uint8_t* ra = cls + (size_t)a * nkt;
@@ -463,6 +529,22 @@ pair_compact_kernel(const uint8_t* __restrict__ cls, int32_t nqt, int32_t nkt,
     base += total;
   }
   if (threadIdx.x == 0) pair_len[w] = base;
+}
+
+// Both kinds of list in one launch: blocks 0 .. nqt + nkt - 1 compact a row of
+// the class matrix or of its transpose, the next (nqt + 1) / 2 the pair lists.
+__global__ void __launch_bounds__(256)
+lists_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ cls_t, int32_t nqt,
+             int32_t nkt, const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ kv_ptr,
+             int32_t* __restrict__ q_cols, int32_t* __restrict__ kv_rows,
+             const int32_t* __restrict__ q_order, const int32_t* __restrict__ pair_off,
+             int32_t* __restrict__ pair_len, int32_t* __restrict__ pair_ent) {
+  __shared__ int wsum[4];
+  const int b = blockIdx.x;
+  if (b < nqt + nkt)
+    compact_row(cls, cls_t, nqt, nkt, q_ptr, kv_ptr, q_cols, kv_rows, b, wsum);
+  else
+    pair_row(cls, nqt, nkt, q_order, pair_off, pair_len, pair_ent, b - nqt - nkt, wsum);
 }
 
 struct Layout {
@@ -559,10 +641,9 @@ extern "C" int32_t build_block_mask(const int32_t* q_seq_id, int32_t nq, const i
                      cnt_kv);
   hipLaunchKernelGGL(scan_sort_kernel, dim3(2), dim3(kSortThreads), 0, s, cnt_q, cnt_kv, nqt, nkt,
                      q_ptr, kv_ptr, q_order, kv_order, pair_off);
-  hipLaunchKernelGGL(compact_kernel, dim3(nqt + nkt), dim3(256), 0, s, cls, cls_t, nqt, nkt, q_ptr,
-                     kv_ptr, q_cols, kv_rows);
-  hipLaunchKernelGGL(pair_compact_kernel, dim3((nqt + 1) / 2), dim3(256), 0, s, cls, nqt, nkt,
-                     q_order, pair_off, pair_len, pair_ent);
+  hipLaunchKernelGGL(lists_kernel, dim3(nqt + nkt + (nqt + 1) / 2), dim3(256), 0, s, cls, cls_t,
+                     nqt, nkt, q_ptr, kv_ptr, q_cols, kv_rows, q_order, pair_off, pair_len,
+                     pair_ent);
   const int32_t st = pa::launch_status();
   if (st != PA_OK) return st;
   out->nq = nq;
